@@ -1,0 +1,91 @@
+"""ctypes view of ``libstreamkl.so`` (the C ABI in ``include/streamkl.h``).
+
+Argument marshalling only.  The library must have been built (see
+``build_lib.py``); loading fails loudly otherwise -- there is no fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstreamkl.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+GRAD_Q1K1, GRAD_Q2K2, GRAD_ALL = 1, 2, 3
+
+EXPORTS = ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk",
+           "streamkl_bwd_workspace_size", "streamkl_status_str", "streamkl_abi_version")
+
+
+class StreamKLError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where} failed: {status_str(status)} ({status})")
+
+
+_lib = None
+_vp, _fp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def load(path: str = LIB_PATH):
+    """Open the library (once) and declare the exported signatures."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    lib.streamkl_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
+                                 _fp, _fp, _fp, _vp]
+    lib.streamkl_fwd.restype = _i
+    lib.streamkl_bwd.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
+                                 _f, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.streamkl_bwd.restype = _i
+    for name in ("streamkl_bwd_dq", "streamkl_bwd_dk"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
+                       _f, _i, _i, _i, _vp, _vp, _vp]
+        fn.restype = _i
+    lib.streamkl_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    lib.streamkl_bwd_workspace_size.restype = _sz
+    lib.streamkl_status_str.argtypes = [_i]
+    lib.streamkl_status_str.restype = ctypes.c_char_p
+    lib.streamkl_abi_version.argtypes = []
+    lib.streamkl_abi_version.restype = _i
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().streamkl_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return load().streamkl_abi_version()
+
+
+def fwd(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, kl, lse1, lse2, stream):
+    """Raw call with integer addresses; returns the status code."""
+    return load().streamkl_fwd(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype,
+                               kl, lse1, lse2, stream)
+
+
+def bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
+        dq1, dk1, dq2, dk2, workspace, workspace_bytes, stream):
+    return load().streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale,
+                               causal, dtype, grad_mask, dq1, dk1, dq2, dk2, workspace,
+                               workspace_bytes, stream)
+
+
+def bwd_half(which, q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype,
+             grad_mask, out1, out2, stream):
+    """streamkl_bwd_dq (which='dq') or streamkl_bwd_dk (which='dk')."""
+    fn = getattr(load(), f"streamkl_bwd_{which}")
+    return fn(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
+              out1, out2, stream)
+
+
+def bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask):
+    return load().streamkl_bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask)

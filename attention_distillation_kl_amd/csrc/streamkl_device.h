@@ -1,0 +1,108 @@
+// streamkl_device.h -- gfx950 building blocks shared by the StreamKL kernels.
+//
+// Matrix-core conventions (CDNA3/CDNA4 32x32 MFMA, wave64):
+//   * A operand (M x K): lane L supplies row m = L % 32 and a run of K values
+//     picked by its half h = L / 32; B operand (K x N): lane L supplies column
+//     n = L % 32 and the same run of K values.
+//   * C/D (32 x 32 fp32, 16 registers): lane L holds column n = L % 32 and rows
+//     m(r, h) = (r / 4) * 8 + 4 h + (r % 4), r = 0..15.
+// Scores are produced with the "stationary" operand (the tensor whose rows the
+// workgroup owns: queries in the forward and dQ kernels, keys in the dK kernel)
+// as the B operand, so that each lane owns one stationary row and 16 streamed
+// rows of every 32 x 32 score block.  Row reductions are then in-lane, and the
+// score block feeds the gradient product directly as a B operand.
+//
+// Element types: bf16 uses v_mfma_f32_32x32x16_bf16 (8 values per lane per
+// product); fp32 uses v_mfma_f32_32x32x2_f32 (1 value per lane per product).
+// A lane always holds half of a row (d/2 elements) as 16-byte chunks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace streamkl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Geometry of one row of d elements stored as 16-byte chunks.
+template <bool BF16, int D>
+struct RowGeom {
+  static constexpr int kElemBytes = BF16 ? 2 : 4;
+  static constexpr int kRowBytes = D * kElemBytes;
+  static constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per row
+  static constexpr int kLaneChunks = kChunks / 2;   // chunks one lane holds
+  static constexpr int kElemsPerChunk = 16 / kElemBytes;
+};
+
+// Which logical chunk of a row lane-half h holds as its c-th fragment chunk.
+// bf16: product c covers d = 16c..16c+15 and half h supplies d = 16c+8h..+7.
+// fp32: half h supplies the contiguous half d in [h*D/2, (h+1)*D/2); chunk c
+// carries 4 consecutive k values consumed by 4 successive 32x32x2 products.
+template <bool BF16, int D>
+__device__ __forceinline__ int frag_chunk(int h, int c) {
+  if constexpr (BF16) return 2 * c + h;
+  else return h * RowGeom<BF16, D>::kLaneChunks + c;
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS row so that 16 lanes reading the
+// same logical chunk of 16 consecutive rows hit 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (CPR >= 16) return c ^ (row & 15);
+  else if constexpr (CPR == 8) return c ^ ((row >> 1) & 7);
+  else if constexpr (CPR == 4) return c ^ ((row >> 2) & 3);
+  else return c;
+}
+
+// acc += A(chunk a) * B(chunk b) over the k values the chunks carry.
+template <bool BF16>
+__device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x16 &acc) {
+  if constexpr (BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[i]),
+                                                __builtin_bit_cast(float, b[i]), acc, 0, 0, 0);
+  }
+}
+
+// Row index (within a 32-row block) of accumulator register r for half h.
+__device__ __forceinline__ int c_row(int r, int h) { return (r >> 2) * 8 + 4 * h + (r & 3); }
+
+// Position of streamed row o (0..15 inside a 16-row group) in the transposed
+// LDS layout.  Lane-half h consumes positions 8h..8h+7 of a group as one run,
+// which are the rows c_row(j, h) for j = 0..7 (the rows its score registers
+// hold), so the gradient product reads one contiguous run per lane.
+__device__ __forceinline__ int tpos(int o) { return 8 * ((o >> 2) & 1) + 4 * (o >> 3) + (o & 3); }
+
+// Map the hardware workgroup id to a logical one so that consecutive logical
+// ids run on the same XCD (workgroups are dealt round-robin over 8 XCDs):
+// all query blocks of one head then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n >> 3;
+  const int full = per << 3;
+  if (b >= full) return b;
+  return (b & 7) * per + (b >> 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Pack two fp32 values to bf16 (round to nearest even) in one dword.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+}  // namespace streamkl

@@ -1,0 +1,32 @@
+// streamkl_launch.h -- internal interface between the C ABI layer and the
+// kernel translation units.  Arguments are validated before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace streamkl {
+
+struct FwdArgs {
+  const void *q1, *k1, *q2, *k2;
+  float *kl, *lse1, *lse2;
+  int bh, nq, nk, d;
+  float scale;
+  bool causal, bf16;
+};
+
+struct BwdArgs {
+  const void *q1, *k1, *q2, *k2;
+  const float *kl, *lse1, *lse2, *dkl;
+  void *dq1, *dk1, *dq2, *dk2;
+  int bh, nq, nk, d;
+  float scale;
+  bool causal, bf16;
+  int grad_mask;  // 1: dq1/dk1, 2: dq2/dk2, 3: both
+};
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
+
+}  // namespace streamkl

@@ -1,0 +1,180 @@
+"""Benchmark: StreamKL fused attention-KL forward + recompute backward on one GPU.
+
+One step = the whole hot path over one batch: the forward kernel (per-row
+KL, LSE1, LSE2), then the two backward kernels (dK1/dK2 and dQ1/dQ2), on
+synthetic inputs already resident in HBM.  Prints ONE JSON line on stdout.
+
+Default workload: B=1, H=32, N_Q=N_K=32768, d=128, bf16, causal, teacher
+Q1,K1 ~ N(0,1), student = teacher + 0.2 N(0,1).  Credited work per head:
+forward 4 N_Q N_K d, forward+backward 16 N_Q N_K d, halved when causal.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q1, k1, q2, k2, target_s):
+    """Time the fp64 oracle (as it stands) on the last query rows of head 0."""
+    import numpy as np
+    import torch
+    import oracle
+
+    c = [t[0, 0].to("cpu", torch.float64).numpy() for t in (q1, k1, q2, k2)]
+
+    def run(rows):
+        rb = w.NQ - rows
+        t0 = time.perf_counter()
+        oracle.head(*c, w.scale, w.causal, rows=(rb, w.NQ), grads=True)
+        dt = time.perf_counter() - t0
+        off = w.NK - w.NQ
+        keys = np.array([min(w.NK, i + off + 1) if w.causal else w.NK for i in range(rb, w.NQ)], dtype=np.float64)
+        return dt, 16.0 * w.d * keys.sum()
+
+    probe = 16
+    dt, _ = run(probe)
+    rows = int(max(probe, min(w.NQ, probe * target_s / max(dt, 1e-3))))
+    dt, flops = run(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle, forward+backward of the last {rows} query rows of head 0 "
+                      f"({flops / 1e12:.3f} TFLOP credited, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-head work is independent and would shard over heads with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_distillation_kl_amd import WORKLOADS, workload_inputs
+    from attention_distillation_kl_amd import ops
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: workload {w.name} {w.as_dict()}")
+    q1, k1, q2, k2 = workload_inputs(w, dev)
+    B, H, NQ, NK, d = w.B, w.H, w.NQ, w.NK, w.d
+    kl = torch.empty(B, H, NQ, device=dev, dtype=torch.float32)
+    lse1, lse2 = torch.empty_like(kl), torch.empty_like(kl)
+    dq = (torch.empty_like(q1), torch.empty_like(q2))
+    dk = (torch.empty_like(k1), torch.empty_like(k2))
+    do_bwd = w.passes == "fwd+bwd"
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kl_, l1_, l2_ = ops.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
+        if ev is not None:
+            ev[1].record()
+        if do_bwd:
+            ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dk)
+            if ev is not None:
+                ev[2].record()
+            ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dq)
+            if ev is not None:
+                ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done")
+
+    nev = 4 if do_bwd else 2
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"bench: {args.steps} timed steps done in {wall:.3f} s")
+
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[nev - 1]) for e in events) / args.steps
+    kern = {"fwd": fwd_ms}
+    if do_bwd:
+        kern["bwd_dk"] = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+        kern["bwd_dq"] = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    fwd_fl = w.fwd_flops()
+    total_fl = w.fwdbwd_flops() if do_bwd else fwd_fl
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    value = total_fl / (step_ms * 1e-3) / 1e12
+    fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
+
+    # Dominant kernel: the one with the largest average duration.  Its MFMA
+    # work per launch: forward 4 N_Q N_K d per head; each backward kernel
+    # recomputes both score blocks (4) and forms two gradients (4): 8 N_Q N_K d.
+    per_launch = {"fwd": fwd_fl, "bwd_dk": 2 * fwd_fl, "bwd_dq": 2 * fwd_fl}
+    dom = max(kern, key=kern.get)
+    ach = per_launch[dom] / (kern[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": None,
+            "flops_per_launch": per_launch[dom], "avg_launch_ms": round(kern[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle sample")
+        cpu = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
+        cpu["value"] = round(cpu["value"], 6)
+
+    desc = (f"{w.name}: B={B},H={H},N_Q={NQ},N_K={NK},d={d},{w.dtype},"
+            f"{'causal' if w.causal else 'non-causal'},{w.mode}" + (f" sigma={w.sigma}" if w.mode == "student" else ""))
+    out = {
+        "metric": "fused attention-KL TFLOP/s (fwd, fwd+bwd) at N=32K causal; % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian teacher, student = teacher + noise)",
+        "config": {"workload": desc, "passes": w.passes, "seed": w.seed, "scale": w.scale},
+        "fwd_tflops": round(fwd_tf, 2),
+        "pct_peak_fwd": round(100 * fwd_tf / peak, 2),
+        "pct_peak_fwdbwd": round(100 * value / peak, 2),
+        "event_ms_per_step": round(step_ms, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * streamkl.h -- C ABI of libstreamkl: fused attention-KL divergence between a
+ * teacher and a student attention distribution, forward and recompute
+ * backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * The method is StreamKL as summarised on gist.science (paper 2606.20005):
+ * for each query row i of each attention head,
+ *
+ *   S_t = scale * Q_t K_t^T        (t = 1 teacher, t = 2 student)
+ *   P_t = softmax(S_t) over the allowed keys of the row
+ *   KL[i] = KL(P1[i,:] || P2[i,:])
+ *
+ * computed in one pass over key tiles with five running row scalars
+ * (two running maxima, two running exponential sums and one accumulator of
+ * the P1-weighted logit difference), finalised as KL = acc/l1 + LSE2 - LSE1
+ * with LSE_t = m_t + log l_t ("Formulazione Online", forward pass section).
+ * The N_Q x N_K matrices P1, P2 are never written to memory.  The backward
+ * pass keeps only KL, LSE1 and LSE2 per row and regenerates
+ * P_t = exp(S_t - LSE_t) tile by tile ("Strategia di Ricalcolo", backward
+ * pass section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout    q1, q2: [B, H, N_Q, d]; k1, k2: [B, H, N_K, d]; contiguous, d
+ *            innermost.  Row vectors kl, lse1, lse2, dkl: [B, H, N_Q] float32.
+ *            Gradients have the shape and element type of the tensor they
+ *            differentiate.
+ *  Element   STREAMKL_BF16 (bfloat16 storage; products accumulate in fp32) or
+ *  types     STREAMKL_F32.  KL and LSE are always float32.
+ *  Logits    natural-log units of the scaled scores: LSE_t = log sum_j
+ *            exp(scale * <q_t[i], k_t[j]>).  One scale for both
+ *            distributions (fold a teacher temperature into q1).
+ *  Causal    key j is allowed for query i iff j <= i + (N_K - N_Q), i.e. the
+ *            mask is aligned to the bottom-right corner (j <= i when
+ *            N_Q == N_K).  Requires N_Q <= N_K so every row has a key.
+ *  Pointers  every tensor pointer is a DEVICE pointer owned by the caller and
+ *            must be 16-byte aligned.  The library never allocates, frees or
+ *            keeps device memory and holds no global mutable state.  Outputs
+ *            are fully overwritten and must not alias inputs.
+ *  Streams   `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *            enqueued asynchronously; nothing synchronises the host.
+ *  Errors    argument errors are reported before anything is enqueued; a
+ *            failed launch (or no usable GPU) returns STREAMKL_ERR_HIP.
+ *            Non-finite input values are not checked; they propagate.
+ */
+#ifndef STREAMKL_H
+#define STREAMKL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STREAMKL_OK = 0,
+  STREAMKL_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, scale, mask, ... */
+  STREAMKL_ERR_UNSUPPORTED = 2,      /* d not in {64, 128} or unknown dtype */
+  STREAMKL_ERR_WORKSPACE = 3,        /* workspace smaller than required     */
+  STREAMKL_ERR_HIP = 4               /* HIP runtime / launch failure         */
+} streamkl_status;
+
+typedef enum { STREAMKL_F32 = 0, STREAMKL_BF16 = 1 } streamkl_dtype;
+
+/* Which gradients the backward pass produces (the page's two
+ * configurations; the two sets are independent partial derivatives). */
+enum {
+  STREAMKL_GRAD_Q1K1 = 1, /* Configuration 2: P2 held fixed, train P1 -> dq1, dk1 */
+  STREAMKL_GRAD_Q2K2 = 2, /* Configuration 1: P1 held fixed, train P2 -> dq2, dk2 */
+  STREAMKL_GRAD_ALL = 3
+};
+
+/*
+ * streamkl_fwd -- forward pass ("Formulazione Online", forward pass section).
+ *   in : q1, k1, q2, k2 (dtype), sizes B, H, N_Q, N_K, d, scale (> 0, finite),
+ *        causal (0/1).
+ *   out: kl[B,H,N_Q]   = KL(P1 || P2) per row (not clamped at 0),
+ *        lse1, lse2    = log-sum-exp of the scaled teacher / student logits.
+ * Causal key tiles beyond a query block's frontier are skipped, not masked.
+ * B*H*N_Q == 0 is a valid no-op.
+ */
+streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2,
+                             const void *k2, int B, int H, int N_Q, int N_K,
+                             int d, float scale, int causal, int dtype,
+                             float *kl, float *lse1, float *lse2, void *stream);
+
+/*
+ * streamkl_bwd_workspace_size -- bytes of device workspace streamkl_bwd needs
+ * for these arguments.  The two-kernel recompute backward needs none (0).
+ */
+size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
+                                   int causal, int dtype, int grad_mask);
+
+/*
+ * streamkl_bwd -- recompute backward pass ("Strategia di Ricalcolo", backward
+ * pass section).  Regenerates P_t = exp(S_t - LSE_t) from the saved row
+ * vectors and forms, for the upstream per-row gradient g = dkl (NULL = ones):
+ *   dS2 = g (P2 - P1)                      (Configuration 1)
+ *   dS1 = g P1 (S1 - S2 - (KL + LSE1 - LSE2))
+ *       = g P1 (log P1 - log P2 - KL)      (Configuration 2; formed from
+ *                                           logits and LSEs, never log P)
+ *   dq_t = scale dS_t k_t,  dk_t = scale dS_t^T q_t.
+ *   in : the forward inputs, kl/lse1/lse2 exactly as streamkl_fwd wrote them,
+ *        dkl [B,H,N_Q] float32 or NULL, grad_mask (STREAMKL_GRAD_*).
+ *   out: dq1, dk1 (required iff grad_mask has Q1K1), dq2, dk2 (iff Q2K2);
+ *        pointers of unrequested gradients may be NULL and are not touched.
+ *   workspace / workspace_bytes: at least streamkl_bwd_workspace_size(...)
+ *        bytes (may be NULL when that is 0).
+ * With N_Q == 0 the key gradients are written as zeros.
+ */
+streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
+                             const void *k2, const float *kl,
+                             const float *lse1, const float *lse2,
+                             const float *dkl, int B, int H, int N_Q, int N_K,
+                             int d, float scale, int causal, int dtype,
+                             int grad_mask, void *dq1, void *dk1, void *dq2,
+                             void *dk2, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * streamkl_bwd_dq / streamkl_bwd_dk -- the two halves of streamkl_bwd, for
+ * callers that schedule them separately (e.g. on two streams).  Same
+ * arguments, meaning and errors as streamkl_bwd, restricted to the query
+ * gradients (dq1, dq2) or to the key gradients (dk1, dk2).  streamkl_bwd is
+ * exactly streamkl_bwd_dk followed by streamkl_bwd_dq on one stream.  The
+ * page describes this split as the fallback of its fused backward when
+ * atomic contention on dQ is high ("Strategia di Ricalcolo", kernel fusion
+ * bullet).  Neither half needs workspace.
+ */
+streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2,
+                                const void *k2, const float *kl,
+                                const float *lse1, const float *lse2,
+                                const float *dkl, int B, int H, int N_Q,
+                                int N_K, int d, float scale, int causal,
+                                int dtype, int grad_mask, void *dq1, void *dq2,
+                                void *stream);
+streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2,
+                                const void *k2, const float *kl,
+                                const float *lse1, const float *lse2,
+                                const float *dkl, int B, int H, int N_Q,
+                                int N_K, int d, float scale, int causal,
+                                int dtype, int grad_mask, void *dk1, void *dk2,
+                                void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *streamkl_status_str(int status);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int streamkl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_H */

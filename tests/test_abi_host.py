@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function ``include/streamkl.h``
+declares, and reject bad arguments with the documented status before it
+enqueues anything.  Pointers passed here are fake (never dereferenced): every
+call below returns during validation, or -- on a host without a GPU -- at the
+launch, with STREAMKL_ERR_HIP.
+"""
+import os
+import re
+
+import pytest
+
+from attention_distillation_kl_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamkl.h")
+
+A = 0x10000       # fake 16-byte aligned device addresses
+A2, A3, A4 = 0x20000, 0x30000, 0x40000
+O1, O2, O3 = 0x50000, 0x60000, 0x70000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int|streamkl_status)\s*\**\s*(streamkl_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert _lib.abi_version() == 1
+    names = ["STREAMKL_OK", "STREAMKL_ERR_INVALID_ARGUMENT", "STREAMKL_ERR_UNSUPPORTED",
+             "STREAMKL_ERR_WORKSPACE", "STREAMKL_ERR_HIP"]
+    for code, name in enumerate(names):
+        assert _lib.status_str(code) == name
+        assert name in open(HEADER).read()
+    assert _lib.status_str(99) == "STREAMKL_ERR_UNKNOWN"
+
+
+def fwd(**kw):
+    a = dict(q1=A, k1=A2, q2=A3, k2=A4, B=1, H=2, NQ=64, NK=64, d=128, scale=0.125, causal=1,
+             dtype=_lib.BF16, kl=O1, lse1=O2, lse2=O3, stream=None)
+    a.update(kw)
+    return _lib.fwd(a["q1"], a["k1"], a["q2"], a["k2"], a["B"], a["H"], a["NQ"], a["NK"], a["d"],
+                    a["scale"], a["causal"], a["dtype"], a["kl"], a["lse1"], a["lse2"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q1=A, k1=A2, q2=A3, k2=A4, kl=O1, lse1=O2, lse2=O3, dkl=None, B=1, H=2, NQ=64, NK=64,
+             d=128, scale=0.125, causal=1, dtype=_lib.BF16, mask=3, dq1=0x80000, dk1=0x90000,
+             dq2=0xA0000, dk2=0xB0000, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return _lib.bwd(a["q1"], a["k1"], a["q2"], a["k2"], a["kl"], a["lse1"], a["lse2"], a["dkl"],
+                    a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["scale"], a["causal"], a["dtype"],
+                    a["mask"], a["dq1"], a["dk1"], a["dq2"], a["dk2"], a["ws"], a["wsb"], a["stream"])
+
+
+INV, UNS = _lib.ERR_INVALID_ARGUMENT, _lib.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNS), (dict(d=256), UNS), (dict(dtype=7), UNS),
+    (dict(scale=0.0), INV), (dict(scale=-1.0), INV), (dict(scale=float("inf")), INV),
+    (dict(scale=float("nan")), INV),
+    (dict(B=-1), INV), (dict(NQ=-3), INV), (dict(NK=-1), INV), (dict(d=-64), INV),
+    (dict(NQ=65, NK=64), INV),            # causal with more queries than keys
+    (dict(NK=0), INV),                    # rows with no keys
+    (dict(causal=2), INV),
+    (dict(q1=None), INV), (dict(k2=None), INV), (dict(kl=None), INV), (dict(lse2=None), INV),
+    (dict(q2=A3 + 8), INV), (dict(lse1=O2 + 4), INV),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=0), INV), (dict(mask=4), INV),
+    (dict(mask=1, dq1=None), INV), (dict(mask=1, dk1=None), INV),
+    (dict(mask=2, dq2=None), INV), (dict(mask=2, dk2=None), INV),
+    (dict(lse1=None), INV), (dict(dkl=O1 + 4), INV), (dict(dk2=0xB0008), INV),
+    (dict(d=32), UNS), (dict(scale=0.0), INV), (dict(NQ=70, NK=64), INV),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, status):
+    assert bwd(**kw) == status
+
+
+def test_empty_problems_are_noops(lib):
+    # Nothing to do: returns OK without touching the GPU.
+    assert fwd(B=0) == _lib.OK
+    assert fwd(NQ=0, kl=None, lse1=None, lse2=None, q1=None, q2=None) == _lib.OK
+    assert fwd(H=0, NK=0) == _lib.OK
+    assert bwd(B=0) == _lib.OK
+    assert bwd(NQ=0, NK=0, q1=None, k1=None, q2=None, k2=None, kl=None, lse1=None, lse2=None,
+               dq1=None, dk1=None, dq2=None, dk2=None) == _lib.OK
+
+
+def test_workspace_query_is_zero_for_two_kernel_backward(lib):
+    for mask in (1, 2, 3):
+        assert _lib.bwd_workspace_size(2, 32, 8192, 8192, 128, 1, _lib.BF16, mask) == 0
+
+
+def test_unrequested_gradients_may_be_null(lib, no_gpu):
+    assert bwd(mask=1, dq2=None, dk2=None) == _lib.ERR_HIP
+    assert bwd(mask=2, dq1=None, dk1=None) == _lib.ERR_HIP
+
+
+@pytest.fixture
+def no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the no-device path cannot be exercised")
+
+
+def test_valid_call_without_gpu_reports_hip_error(lib, no_gpu):
+    assert fwd() == _lib.ERR_HIP
+    assert fwd(dtype=_lib.F32, d=64, causal=0, NQ=100, NK=37) == _lib.ERR_HIP
+    assert bwd() == _lib.ERR_HIP
+    assert bwd(NQ=0, q1=None, q2=None, kl=None, lse1=None, lse2=None, dq1=None, dq2=None) == _lib.ERR_HIP
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from attention_distillation_kl_amd import ops
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        ops.streamkl_fwd(x, x, x, x)
