@@ -384,7 +384,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
               for (int j = 0; j < 8; ++j)
                 acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    __builtin_bit_cast(float, j < 4 ? a0[j] : a1[j - 4]), ds1[8 * ks + j], acc1[mb], 0, 0, 0);
+                    u2f(j < 4 ? a0[j] : a1[j - 4]), ds1[8 * ks + j], acc1[mb], 0, 0, 0);
             }
             if (kG2) {
               const u32x4 a0 = base[C::kOffT2 + drow * C::kTCPR + pc0];
@@ -392,7 +392,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
               for (int j = 0; j < 8; ++j)
                 acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    __builtin_bit_cast(float, j < 4 ? a0[j] : a1[j - 4]), ds2[8 * ks + j], acc2[mb], 0, 0, 0);
+                    u2f(j < 4 ? a0[j] : a1[j - 4]), ds2[8 * ks + j], acc2[mb], 0, 0, 0);
             }
           }
         }

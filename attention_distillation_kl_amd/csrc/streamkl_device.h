@@ -63,6 +63,11 @@ __device__ __forceinline__ int swz(int row, int c) {
   else return c;
 }
 
+// Reinterpret a 32-bit word as fp32.  Always pass the word by value: clang
+// mis-evaluates __builtin_bit_cast applied directly to an ext_vector element
+// (it reads element 0), which is why the element is copied into `x` first.
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // acc += A(chunk a) * B(chunk b) over the k values the chunks carry.
 template <bool BF16>
 __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x16 &acc) {
@@ -72,8 +77,7 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x1
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[i]),
-                                                __builtin_bit_cast(float, b[i]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(u2f(a[i]), u2f(b[i]), acc, 0, 0, 0);
   }
 }
 

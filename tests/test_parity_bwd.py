@@ -174,3 +174,16 @@ def test_autograd_function_matches_direct_calls():
     assert torch.equal(kl.detach(), kl_d)
     for x, gd in zip(xs, grads):
         assert torch.equal(x.grad, gd)
+
+
+def test_bwd_halves_match_full_backward():
+    """streamkl_bwd == streamkl_bwd_dk then streamkl_bwd_dq, bit for bit."""
+    q1, k1, q2, k2 = make_inputs(1, 2, 260, 300, 128, torch.bfloat16, "student", 0.3, seed=17, device=DEV)
+    g = upstream_grad(1, 2, 260, seed=17, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 0.1, True)
+    full = ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, 0.1, True)
+    dk1, dk2 = ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl, l1, l2, g, 0.1, True)
+    dq1, dq2 = ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl, l1, l2, g, 0.1, True)
+    torch.cuda.synchronize()
+    for a, b in zip(full, (dq1, dk1, dq2, dk2)):
+        assert torch.equal(a, b)

@@ -16,7 +16,7 @@ DEV = "cuda"
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def run_and_compare(q1, k1, q2, k2, scale, causal, heads=None, tag=""):
+def run_and_compare(q1, k1, q2, k2, scale, causal, heads=None, tag="", by_magnitude=False):
     kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
     torch.cuda.synchronize()
     B, H = q1.shape[:2]
@@ -25,8 +25,9 @@ def run_and_compare(q1, k1, q2, k2, scale, causal, heads=None, tag=""):
     worst = 0.0
     for hh in heads:
         b, h = divmod(hh, H)
+        mag = np.maximum(np.abs(ref[hh]["lse1"]), np.abs(ref[hh]["lse2"])) if by_magnitude else None
         for name, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
-            worst = max(worst, check_rows(to64(got[b, h]), ref[hh][name], q1.dtype, f"{tag} head {hh} {name}"))
+            worst = max(worst, check_rows(to64(got[b, h]), ref[hh][name], q1.dtype, f"{tag} head {hh} {name}", mag))
     return kl, l1, l2, worst
 
 
@@ -117,12 +118,13 @@ def test_fwd_uniform_student():
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_fwd_peaked_and_large_inputs(dt):
     """scale = 1 on N(0, 1) d = 128 data gives logits with std ~11 (near one-hot
-    rows); x8 inputs on top of that stress the max-shift."""
+    rows); x8 inputs on top of that stress the max-shift.  Logits reach tens
+    to hundreds here, so the fp32 bound is taken relative to max |LSE|."""
     q1, k1, q2, k2 = make_inputs(1, 2, 256, 256, 128, DT[dt], "student", 0.3, seed=8, device=DEV)
-    kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, True, tag="peaked")
+    kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, True, tag="peaked", by_magnitude=True)
     assert torch.isfinite(kl).all()
     big = [t * 8 for t in (q1, k1, q2, k2)]
-    kl, _, _, _ = run_and_compare(*big, 0.5, False, tag="large")
+    kl, _, _, _ = run_and_compare(*big, 0.5, False, tag="large", by_magnitude=True)
     assert torch.isfinite(kl).all()
 
 
