@@ -24,17 +24,22 @@
 // Both recompute S1, S2; neither needs atomics or workspace, and results are
 // bitwise deterministic.
 //
-// Per 32-row streamed tile each wave:
+// Per 32-row block of a streamed tile, each wave:
 //   1. S_t^T block (32 streamed x 32 stationary) = Y_t X_t^T with the
-//      stationary fragments X_t held in registers (B operand) and the
-//      streamed rows Y_t read from LDS (A operand): each lane owns one
-//      stationary row and 16 streamed rows of the block;
-//   2. P_t = exp2(s_t * scale*log2e - LSE_t*log2e + log2|g|), dS_t in fp32;
-//   3. dX_t^T (d x 32 stationary) += Y_t^T dS_t, with Y_t^T read from a
-//      transposed LDS copy whose row order matches the register order of dS
-//      (so dS feeds the product as the B operand with no shuffles).
-// The sign of g is applied to dQ at the end (ROLE_DQ) or folded into the
-// transposed query copy (ROLE_DK); |g| is folded into the exponent.
+//      stationary fragments X_t in registers (B operand) and the streamed
+//      rows Y_t read from LDS (A operand): each lane owns one stationary row
+//      and 16 streamed rows of the block;
+//   2. P_t = exp2(s_t * scale*log2e - LSE_t*log2e) and, with raw dot products
+//      s_t and delta' = delta / scale,
+//        e2 = P2 - P1           (dS2 = g e2)
+//        e1 = P1 (s1 - s2 - delta')    (dS1 = g scale e1),
+//      g multiplied in per element only where it varies along the block's
+//      rows (ROLE_DK with an upstream gradient), otherwise at the end;
+//   3. dX_t^T (d x 32 stationary) += Y_t^T e_t: the A operand Y_t^T is read
+//      from the same row-major LDS tile with transposing reads
+//      (ds_read_b64_tr_b16), in the row order of e_t's registers, so e_t feeds
+//      the product as the B operand with no shuffles.
+// Tiles arrive in LDS by direct global->LDS copies, double buffered.
 #pragma once
 
 #include "streamkl_device.h"
@@ -52,51 +57,49 @@ struct BwdCfg {
   using G = RowGeom<BF16, D>;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBS = 32 * kWaves;   // stationary rows per workgroup
-  static constexpr int kBT = 32;            // streamed rows per LDS tile
-  static constexpr int kRowChunks = kBT * G::kChunks;             // row-major copy, per tensor
-  static constexpr int kTCPR = kBT * G::kElemBytes / 16;          // chunks per transposed row
-  static constexpr int kTChunks = D * kTCPR;                      // transposed copy, per tensor
-  static constexpr int kCstChunks = 3 * kBT / 4;                  // 3 fp32 arrays of kBT
-  // stage layout in 16-B chunks: [Y1][Y2][Y1^T][Y2^T][L1'|L2'|delta]
-  static constexpr int kOffY2 = kRowChunks;
-  static constexpr int kOffT1 = 2 * kRowChunks;
-  static constexpr int kOffT2 = 2 * kRowChunks + kTChunks;
-  static constexpr int kOffCst = 2 * kRowChunks + 2 * kTChunks;
-  static constexpr int kStage = kOffCst + kCstChunks;
+  static constexpr int kBS = 32 * kWaves;                 // stationary rows per workgroup
+  static constexpr int kBT = BF16 ? 64 : 32;              // streamed rows per LDS tile
+  static constexpr int kSub = kBT / 32;                   // 32-row blocks per tile
+  static constexpr int kTileChunks = kBT * G::kChunks;    // 16-B chunks per tensor tile
+  static constexpr int kLoads = kTileChunks / kThreads;   // copies per thread per tensor
+  static constexpr int kNCst = 4;                         // per-row constant arrays
+  static constexpr int kOffY2 = kTileChunks;
+  static constexpr int kOffCst = 2 * kTileChunks;
+  static constexpr int kStage = kOffCst + kNCst * kBT / 4;
   static constexpr size_t kLdsBytes = size_t(2) * kStage * 16;
-  // staging unit: 4 consecutive streamed rows x one 16-B chunk of one tensor
-  static constexpr int kBlocksPerTensor = (kBT / 4) * G::kChunks;
-  static constexpr int kBlocks = 2 * kBlocksPerTensor;
-  static constexpr int kBlocksPerThread = (kBlocks + kThreads - 1) / kThreads;
+  static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
 struct BwdParams {
   const char *q1, *k1, *q2, *k2;
   const float *kl, *lse1, *lse2, *dkl;
   char *dq1, *dk1, *dq2, *dk2;
-  int nq, nk, nsb;  // nsb: stationary blocks per head
-  float scale, c;   // c = scale * log2(e)
+  int nq, nk, nsb;    // nsb: stationary blocks per head
+  float scale, c;     // c = scale * log2(e)
+  float inv_scale;
 };
 
-// Per-row constants of the recompute: P_t |g| = exp2(s_t c - Lt'),
-// Lt' = LSE_t log2(e) - log2|g|, and delta = KL + LSE1 - LSE2.
-__device__ __forceinline__ void row_constants(const BwdParams &p, size_t i, float &L1, float &L2,
-                                              float &delta, float &sgn) {
-  const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
-  float lg = 0.f;
-  sgn = 1.f;
-  if (p.dkl) {
-    const float g = p.dkl[i];
-    lg = log2f(fabsf(g));  // g == 0 -> -inf -> P|g| = 0
-    sgn = g < 0.f ? -1.f : 1.f;
+// Per-row constants: L_t = LSE_t log2(e) (P_t = exp2(s_t c - L_t)), the
+// upstream gradient g (1 without one), dp = delta / scale and gd = g dp.
+// Rows past N_Q get L = +inf and zeros, so every product they enter is zero.
+struct RowCst {
+  float l1, l2, g, gd, dp;
+};
+
+__device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bool valid) {
+  RowCst r{INFINITY, INFINITY, 0.f, 0.f, 0.f};
+  if (valid) {
+    const float lse1 = p.lse1[i], lse2 = p.lse2[i];
+    r.dp = (p.kl[i] + lse1 - lse2) * p.inv_scale;
+    r.g = p.dkl ? p.dkl[i] : 1.f;
+    r.l1 = lse1 * kLog2e;
+    r.l2 = lse2 * kLog2e;
+    r.gd = r.g * r.dp;
   }
-  L1 = lse1 * kLog2e - lg;
-  L2 = lse2 * kLog2e - lg;
-  delta = kl + lse1 - lse2;
+  return r;
 }
 
-template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK>
+template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<BF16, D>;
@@ -145,9 +148,9 @@ void bwd_kernel(BwdParams p) {
     for (int c = 0; c < G::kLaneChunks; ++c) xf1[c] = xf2[c] = zero4();
   }
 
-  // ROLE_DQ: the lane's query is stationary, its constants live in registers.
-  float rl1 = INFINITY, rl2 = INFINITY, rdelta = 0.f, rsign = 1.f;
-  if (ROLE == ROLE_DQ && srow < p.nq) row_constants(p, size_t(bh) * p.nq + srow, rl1, rl2, rdelta, rsign);
+  // ROLE_DQ: the lane's query is stationary; its constants live in registers.
+  RowCst rc{INFINITY, INFINITY, 0.f, 0.f, 0.f};
+  if (ROLE == ROLE_DQ) rc = row_constants(p, size_t(bh) * p.nq + srow, srow < p.nq);
 
   // Streamed range and per-element admissibility.
   //   ROLE_DQ (streamed keys tau, stationary query sigma): tau <= sigma + off, tau < N_K.
@@ -159,9 +162,9 @@ void bwd_kernel(BwdParams p) {
   }
   const int tile0 = t_begin / C::kBT;
   const int tile1 = (t_end + C::kBT - 1) / C::kBT;
-  int lim;       // ROLE_DQ: last admissible key; ROLE_DK: first admissible query
-  int w_easy;    // wave-uniform bound beyond which no element needs a mask
-  int w_any;     // wave-uniform bound beyond which the whole tile is masked
+  int lim;     // ROLE_DQ: last admissible key; ROLE_DK: first admissible query
+  int w_easy;  // per 32-row block: beyond this no element of the wave needs a mask
+  int w_any;   // per 32-row block: beyond this every element of the wave is masked
   if (ROLE == ROLE_DQ) {
     lim = CAUSAL ? min(srow + off, p.nk - 1) : p.nk - 1;
     w_easy = CAUSAL ? min(w0 + off, p.nk - 1) : p.nk - 1;
@@ -172,107 +175,38 @@ void bwd_kernel(BwdParams p) {
     w_any = CAUSAL ? max(w0 - off, 0) : 0;
   }
 
-  // ---------------------------------------------------------------- staging
-  u32x4 st[C::kBlocksPerThread][4];
-  uint32_t sgnmask[C::kBlocksPerThread][2];  // ROLE_DK: sign of g folded into Y^T
-
-  auto gload = [&](int tile) {
-    const int tb = tile * C::kBT;
+  // ------------------------------------------------------------ staging
+  // Streamed tile `tile` -> LDS buffer `stage` by direct global->LDS copies.
+  // Lane L of wave w fills chunk position i*256 + 64w + L; the global side
+  // picks the (row, logical chunk) stored there (the swizzle is an XOR, its
+  // own inverse).  Rows past the end repeat the last row; they are masked.
+  auto issue = [&](int tile, int stage) {
 #pragma unroll
-    for (int bi = 0; bi < C::kBlocksPerThread; ++bi) {
-      const int blk = tid + bi * C::kThreads;
-      if (blk < C::kBlocks) {
-        const int t = blk / C::kBlocksPerTensor;
-        const int rem = blk - t * C::kBlocksPerTensor;
-        const int rg = rem / G::kChunks, ch = rem - rg * G::kChunks;
-        const char *Y = t ? Y2 : Y1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = tb + 4 * rg + e;
-          st[bi][e] = row < nt ? *reinterpret_cast<const u32x4 *>(Y + size_t(row) * G::kRowBytes + ch * 16)
-                               : zero4();
-        }
-        sgnmask[bi][0] = sgnmask[bi][1] = 0u;
-        if (ROLE == ROLE_DK && p.dkl) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = tb + 4 * rg + e;
-            const bool neg = row < p.nq && p.dkl[size_t(bh) * p.nq + row] < 0.f;
-            if (BF16) sgnmask[bi][e >> 1] |= neg ? (0x8000u << (16 * (e & 1))) : 0u;
-            else sgnmask[bi][0] |= neg ? (1u << e) : 0u;
-          }
-        }
-      }
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int pos = i * C::kThreads + tid;
+      const int row = pos / G::kChunks;
+      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+      const int r = min(tile * C::kBT + row, nt - 1);
+      const size_t o = size_t(r) * G::kRowBytes + ch * 16;
+      u32x4 *base = lds + stage * C::kStage + i * C::kThreads + wave * 64;
+      dma16(Y1 + o, base);
+      dma16(Y2 + o, base + C::kOffY2);
     }
   };
-
-  float cst_l1 = INFINITY, cst_l2 = INFINITY, cst_d = 0.f;  // ROLE_DK row constants in flight
+  RowCst nc{INFINITY, INFINITY, 0.f, 0.f, 0.f};  // ROLE_DK: next tile's row constants
   auto cload = [&](int tile) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
       const int row = tile * C::kBT + tid;
-      float sg;
-      cst_l1 = INFINITY;
-      cst_l2 = INFINITY;
-      cst_d = 0.f;
-      if (row < p.nq) row_constants(p, size_t(bh) * p.nq + row, cst_l1, cst_l2, cst_d, sg);
+      nc = row_constants(p, size_t(bh) * p.nq + row, row < p.nq);
     }
   };
-
-  auto swrite = [&](int stage) {
-    u32x4 *base = lds + stage * C::kStage;
-#pragma unroll
-    for (int bi = 0; bi < C::kBlocksPerThread; ++bi) {
-      const int blk = tid + bi * C::kThreads;
-      if (blk < C::kBlocks) {
-        const int t = blk / C::kBlocksPerTensor;
-        const int rem = blk - t * C::kBlocksPerTensor;
-        const int rg = rem / G::kChunks, ch = rem - rg * G::kChunks;
-        u32x4 *ym = base + (t ? C::kOffY2 : 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 4 * rg + e;
-          ym[row * G::kChunks + swz<G::kChunks>(row, ch)] = st[bi][e];
-        }
-        const bool want_t = t ? kG2 : kG1;
-        if (want_t) {
-          u32x4 *yt = base + (t ? C::kOffT2 : C::kOffT1);
-          // rows 4rg..4rg+3 sit at 4 consecutive positions of the transposed layout
-          const int pos0 = 16 * ((4 * rg) >> 4) + tpos((4 * rg) & 15);
-          if constexpr (BF16) {
-            // element e of the chunk is d = 8 ch + e; pack (row0,row1), (row2,row3)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int w = e >> 1;
-              const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-              uint32_t lo = __builtin_amdgcn_perm(st[bi][1][w], st[bi][0][w], sel);
-              uint32_t hi = __builtin_amdgcn_perm(st[bi][3][w], st[bi][2][w], sel);
-              lo ^= sgnmask[bi][0];
-              hi ^= sgnmask[bi][1];
-              const int drow = 8 * ch + e;
-              const int byte = pos0 * 2;  // 8-B aligned inside a 16-B chunk
-              const int pch = swz<C::kTCPR>(drow, byte >> 4);
-              uint32_t *dst = reinterpret_cast<uint32_t *>(yt + drow * C::kTCPR + pch) + ((byte & 15) >> 2);
-              *reinterpret_cast<u32x2 *>(dst) = u32x2{lo, hi};
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              u32x4 v{st[bi][0][e], st[bi][1][e], st[bi][2][e], st[bi][3][e]};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] ^= ((sgnmask[bi][0] >> q) & 1u) << 31;
-              const int drow = 4 * ch + e;
-              const int pch = swz<C::kTCPR>(drow, pos0 >> 2);
-              yt[drow * C::kTCPR + pch] = v;
-            }
-          }
-        }
-      }
-    }
+  auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
-      float *cst = reinterpret_cast<float *>(base + C::kOffCst);
-      cst[tid] = cst_l1;
-      cst[C::kBT + tid] = cst_l2;
-      cst[2 * C::kBT + tid] = cst_d;
+      float *cst = reinterpret_cast<float *>(lds + stage * C::kStage + C::kOffCst);
+      cst[tid] = nc.l1;
+      cst[C::kBT + tid] = nc.l2;
+      cst[2 * C::kBT + tid] = nc.g;
+      cst[3 * C::kBT + tid] = nc.gd;
     }
   };
 
@@ -283,57 +217,65 @@ void bwd_kernel(BwdParams p) {
     acc2[mb] = f32x16{};
   }
 
-  const float c = p.c, scale = p.scale;
+  const float c = p.c;
   const int ntiles = tile1 - tile0;
   if (ntiles > 0) {
-    gload(tile0);
+    issue(tile0, 0);
     cload(tile0);
-    swrite(0);
+    cstore(0);
   }
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int tile = tile0 + it;
     const int stage = it & 1;
+    // Buffer stage^1 was last read in iteration it-1, which ended in a barrier.
     if (it + 1 < ntiles) {
-      gload(tile + 1);
+      issue(tile + 1, stage ^ 1);
       cload(tile + 1);
     }
-    const int tb = tile * C::kBT;
-    const bool tile_live = ROLE == ROLE_DQ ? tb <= w_any : tb + C::kBT - 1 >= w_any;
+    const u32x4 *ybase = lds + stage * C::kStage;
+    const float *cst = reinterpret_cast<const float *>(ybase + C::kOffCst);
 
-    if (wave_active && tile_live) {
-      const u32x4 *base = lds + stage * C::kStage;
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      const int tb = tile * C::kBT + sb * 32;  // first streamed row of this block
+      const bool live = ROLE == ROLE_DQ ? tb <= w_any : tb + 31 >= w_any;
+      if (!(wave_active && live)) continue;
+
       // 1. recompute the two score blocks
       f32x16 s1 = f32x16{}, s2 = f32x16{};
+      const int arow = sb * 32 + col;
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-        const int pos = col * G::kChunks + swz<G::kChunks>(col, frag_chunk<BF16, D>(h, cc));
-        mfma_chunk<BF16>(base[pos], xf1[cc], s1);
-        mfma_chunk<BF16>(base[C::kOffY2 + pos], xf2[cc], s2);
+        const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
+        mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+        mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
       }
 
-      // 2. regenerate P and form dS (fp32)
+      // 2. regenerate P and form e1, e2 (fp32)
       bool need_mask;
-      if (ROLE == ROLE_DQ) need_mask = tb + C::kBT - 1 > w_easy;
-      else need_mask = (CAUSAL && tb < w_easy) || tb + C::kBT > p.nq;
-      float ds1[16], ds2[16];
-      const float *cst = reinterpret_cast<const float *>(base + C::kOffCst);
+      if (ROLE == ROLE_DQ) need_mask = tb + 31 > w_easy;
+      else need_mask = (CAUSAL && tb < w_easy) || tb + 32 > p.nq;
+      float e1[16], e2[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 L1v, L2v, Dv;
+        f32x4 L1v, L2v, Gv, GDv;
         if (ROLE == ROLE_DK) {
-          const int r0 = g4 * 8 + 4 * h;
+          const int r0 = sb * 32 + g4 * 8 + 4 * h;
           L1v = *reinterpret_cast<const f32x4 *>(cst + r0);
           L2v = *reinterpret_cast<const f32x4 *>(cst + C::kBT + r0);
-          Dv = *reinterpret_cast<const f32x4 *>(cst + 2 * C::kBT + r0);
+          if (GSIGN) Gv = *reinterpret_cast<const f32x4 *>(cst + 2 * C::kBT + r0);
+          GDv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = g4 * 4 + q;
-          const float L1 = ROLE == ROLE_DK ? L1v[q] : rl1;
-          const float L2 = ROLE == ROLE_DK ? L2v[q] : rl2;
-          const float dl = ROLE == ROLE_DK ? Dv[q] : rdelta;
+          const float L1 = ROLE == ROLE_DK ? L1v[q] : rc.l1;
+          const float L2 = ROLE == ROLE_DK ? L2v[q] : rc.l2;
+          // ROLE_DK: g dp of the streamed row (dp itself when there is no g);
+          // ROLE_DQ: dp of the lane's own row, g is applied at write-out.
+          const float gd = ROLE == ROLE_DK ? GDv[q] : rc.dp;
           float p1 = fast_exp2(fmaf(s1[r], c, -L1));
           float p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -L2)) : 0.f;
           if (need_mask) {
@@ -342,70 +284,82 @@ void bwd_kernel(BwdParams p) {
             p1 = ok ? p1 : 0.f;
             p2 = ok ? p2 : 0.f;
           }
-          ds2[r] = p2 - p1;
-          ds1[r] = p1 * fmaf(s1[r] - s2[r], scale, -dl);
+          if (ROLE == ROLE_DK && GSIGN) {
+            e2[r] = (p2 - p1) * Gv[q];
+            e1[r] = p1 * fmaf(s1[r] - s2[r], Gv[q], -gd);
+          } else {
+            e2[r] = p2 - p1;
+            e1[r] = p1 * ((s1[r] - s2[r]) - gd);
+          }
         }
       }
 
-      // 3. gradient products: dX_t^T += Y_t^T dS_t
+      // 3. gradient products: dX_t^T += Y_t^T e_t
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if constexpr (BF16) {
           u32x4 b1, b2;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            b1[w] = pack_bf16(ds1[8 * ks + 2 * w], ds1[8 * ks + 2 * w + 1]);
-            b2[w] = pack_bf16(ds2[8 * ks + 2 * w], ds2[8 * ks + 2 * w + 1]);
+            b1[w] = pack_bf16(e1[8 * ks + 2 * w], e1[8 * ks + 2 * w + 1]);
+            b2[w] = pack_bf16(e2[8 * ks + 2 * w], e2[8 * ks + 2 * w + 1]);
           }
+          // transposing-read supplier: row sb*32 + 16ks + 8t + 4h + s/4,
+          // columns mb*32 + 16(grp&1) + 4(s&3) .. +3   (s = lane % 16, grp = lane / 16)
+          const int s16 = lane & 15, grp = lane >> 4;
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) {
-            const int drow = mb * 32 + col;
-            const int pch = swz<C::kTCPR>(drow, 2 * ks + h);
-            if (kG1) {
-              const u32x4 a = base[C::kOffT1 + drow * C::kTCPR + pch];
+            const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+            u32x4 a1, a2;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+              const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
+              if (kG1) {
+                const u32x2 v = read_tr(reinterpret_cast<const char *>(ybase) + byte);
+                a1[2 * t] = v[0];
+                a1[2 * t + 1] = v[1];
+              }
+              if (kG2) {
+                const u32x2 v = read_tr(reinterpret_cast<const char *>(ybase + C::kOffY2) + byte);
+                a2[2 * t] = v[0];
+                a2[2 * t + 1] = v[1];
+              }
+            }
+            if (kG1)
               acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b1), acc1[mb], 0, 0, 0);
-            }
-            if (kG2) {
-              const u32x4 a = base[C::kOffT2 + drow * C::kTCPR + pch];
+                  __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1), acc1[mb], 0, 0, 0);
+            if (kG2)
               acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b2), acc2[mb], 0, 0, 0);
-            }
+                  __builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b2), acc2[mb], 0, 0, 0);
           }
         } else {
+          const float *yf1 = reinterpret_cast<const float *>(ybase);
+          const float *yf2 = reinterpret_cast<const float *>(ybase + C::kOffY2);
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) {
-            const int drow = mb * 32 + col;
-            const int pc0 = swz<C::kTCPR>(drow, 4 * ks + 2 * h);
-            const int pc1 = swz<C::kTCPR>(drow, 4 * ks + 2 * h + 1);
-            if (kG1) {
-              const u32x4 a0 = base[C::kOffT1 + drow * C::kTCPR + pc0];
-              const u32x4 a1 = base[C::kOffT1 + drow * C::kTCPR + pc1];
+            const int d = mb * 32 + col;
 #pragma unroll
-              for (int j = 0; j < 8; ++j)
-                acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    u2f(j < 4 ? a0[j] : a1[j - 4]), ds1[8 * ks + j], acc1[mb], 0, 0, 0);
-            }
-            if (kG2) {
-              const u32x4 a0 = base[C::kOffT2 + drow * C::kTCPR + pc0];
-              const u32x4 a1 = base[C::kOffT2 + drow * C::kTCPR + pc1];
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    u2f(j < 4 ? a0[j] : a1[j - 4]), ds2[8 * ks + j], acc2[mb], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+              const int row = sb * 32 + 16 * ks + c_row(j, h);
+              const int idx = (row * G::kChunks + swz<G::kChunks>(row, d >> 2)) * 4 + (d & 3);
+              if (kG1) acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf1[idx], e1[8 * ks + j], acc1[mb], 0, 0, 0);
+              if (kG2) acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf2[idx], e2[8 * ks + j], acc2[mb], 0, 0, 0);
             }
           }
         }
       }
     }
 
-    if (it + 1 < ntiles) swrite(stage ^ 1);
-    __syncthreads();
+    if (it + 1 < ntiles) cstore(stage ^ 1);
+    __syncthreads();  // also waits for the copies into stage^1
   }
 
   // ---------------------------------------------------------------- write-out
+  // dS2 = g e2 and dS1 = g scale e1; the gradients carry one more scale.
   if (srow < ns) {
-    const float f = scale * (ROLE == ROLE_DQ ? rsign : 1.f);
+    const float gq = ROLE == ROLE_DQ ? rc.g : 1.f;
+    const float f1 = p.scale * p.scale * gq, f2 = p.scale * gq;
     char *O1 = ROLE == ROLE_DQ ? p.dq1 : p.dk1;
     char *O2 = ROLE == ROLE_DQ ? p.dq2 : p.dk2;
     const size_t ro = (size_t(bh) * ns + srow) * G::kRowBytes;
@@ -414,6 +368,7 @@ void bwd_kernel(BwdParams p) {
       if (t == 0 && !kG1) continue;
       if (t == 1 && !kG2) continue;
       char *O = (t ? O2 : O1) + ro;
+      const float f = t ? f2 : f1;
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -432,7 +387,7 @@ void bwd_kernel(BwdParams p) {
   }
 }
 
-template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK>
+template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   using C = BwdCfg<BF16, D>;
   BwdParams p;
@@ -454,10 +409,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   p.nsb = (ns + C::kBS - 1) / C::kBS;
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
+  p.inv_scale = float(1.0 / double(a.scale));
   const long long blocks = (long long)p.nsb * a.bh;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-  const void *fn = reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK>);
+  const void *fn = reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN>);
   if (C::kLdsBytes > 65536) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(C::kLdsBytes));
     if (e != hipSuccess) return e;
@@ -466,28 +422,28 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   return hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
 }
 
+template <int ROLE, bool BF16, int D, bool CAUSAL>
+hipError_t launch_bwd_masks(const BwdArgs &a, hipStream_t s) {
+  // Only the key-gradient role varies g along a block's rows.
+  const bool gsign = ROLE == ROLE_DK && a.dkl != nullptr;
+  switch (a.grad_mask) {
+    case 1: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, true>(a, s)
+                         : launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, false>(a, s);
+    case 2: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, true>(a, s)
+                         : launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, false>(a, s);
+    default: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, true>(a, s)
+                          : launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, false>(a, s);
+  }
+}
+
 template <int ROLE>
 hipError_t launch_bwd_role(const BwdArgs &a, hipStream_t s) {
-#define STREAMKL_BWD_MASKS(BF, DD, CA)                                  \
-  switch (a.grad_mask) {                                                \
-    case 1: return launch_bwd_t<BF, DD, CA, ROLE, 1>(a, s);             \
-    case 2: return launch_bwd_t<BF, DD, CA, ROLE, 2>(a, s);             \
-    default: return launch_bwd_t<BF, DD, CA, ROLE, 3>(a, s);            \
-  }
   if (a.bf16) {
-    if (a.d == 64) {
-      if (a.causal) { STREAMKL_BWD_MASKS(true, 64, true) } else { STREAMKL_BWD_MASKS(true, 64, false) }
-    } else {
-      if (a.causal) { STREAMKL_BWD_MASKS(true, 128, true) } else { STREAMKL_BWD_MASKS(true, 128, false) }
-    }
-  } else {
-    if (a.d == 64) {
-      if (a.causal) { STREAMKL_BWD_MASKS(false, 64, true) } else { STREAMKL_BWD_MASKS(false, 64, false) }
-    } else {
-      if (a.causal) { STREAMKL_BWD_MASKS(false, 128, true) } else { STREAMKL_BWD_MASKS(false, 128, false) }
-    }
+    if (a.d == 64) return a.causal ? launch_bwd_masks<ROLE, true, 64, true>(a, s) : launch_bwd_masks<ROLE, true, 64, false>(a, s);
+    return a.causal ? launch_bwd_masks<ROLE, true, 128, true>(a, s) : launch_bwd_masks<ROLE, true, 128, false>(a, s);
   }
-#undef STREAMKL_BWD_MASKS
+  if (a.d == 64) return a.causal ? launch_bwd_masks<ROLE, false, 64, true>(a, s) : launch_bwd_masks<ROLE, false, 64, false>(a, s);
+  return a.causal ? launch_bwd_masks<ROLE, false, 128, true>(a, s) : launch_bwd_masks<ROLE, false, 128, false>(a, s);
 }
 
 }  // namespace streamkl

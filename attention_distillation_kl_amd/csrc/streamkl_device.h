@@ -53,13 +53,15 @@ __device__ __forceinline__ int frag_chunk(int h, int c) {
   else return h * RowGeom<BF16, D>::kLaneChunks + c;
 }
 
-// XOR swizzle of 16-byte chunks inside an LDS row so that 16 lanes reading the
-// same logical chunk of 16 consecutive rows hit 16 distinct bank groups.
+// XOR swizzle of the 16-byte chunks of an LDS row: chunk c of row r is stored
+// at c ^ sigma(r).  sigma is a bijection on 16 consecutive rows, so 16 lanes
+// reading one logical chunk of 16 consecutive rows hit 16 distinct bank
+// groups; and for 8 consecutive rows x 4 consecutive chunks (the footprint of
+// a transposing read, see read_tr below) every bank group is hit exactly twice.
 template <int CPR>
 __device__ __forceinline__ int swz(int row, int c) {
-  if constexpr (CPR >= 16) return c ^ (row & 15);
-  else if constexpr (CPR == 8) return c ^ ((row >> 1) & 7);
-  else if constexpr (CPR == 4) return c ^ ((row >> 2) & 3);
+  if constexpr (CPR >= 16) return c ^ (4 * (row & 3) + ((row >> 2) & 3));
+  else if constexpr (CPR == 8) return c ^ (4 * ((row >> 1) & 1) + ((row >> 2) & 3));
   else return c;
 }
 
@@ -101,6 +103,34 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// NaN-propagating maximum (IEEE 754-2019 maximum).  gfx950 executes it
+// natively (v_maximum3_f32), without the per-input NaN quieting that fmaxf
+// (maxNum) needs in IEEE mode.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
+typedef short lds_v4s __attribute__((vector_size(8)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive 16-bit values M[s][0..3]; lane
+// i = 4a + b receives M[a][b], M[4+a][b], M[8+a][b], M[12+a][b].  With
+// M[s] = row (base + s/4) of a row-major bf16 tile, columns d0(s%4)..+3, lane
+// i gets column d0(a) + b of 4 consecutive rows: a K-major MFMA operand read
+// straight from an N-major tile.
+__device__ __forceinline__ u32x2 read_tr(const void *lds_byte_addr) {
+  typedef __attribute__((address_space(3))) lds_v4s lds_v4s_ptr;
+  const auto *p = (const lds_v4s_ptr *)(__attribute__((address_space(3))) char *)(lds_byte_addr);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr *)p));
+}
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane L
+// of the wave writes its 16 bytes to lds_wave_base + 16 L.  `lds_wave_base`
+// must be the same for the whole wave.  Completion is tracked by vmcnt, so a
+// __syncthreads() (which waits for it) orders it before later LDS reads.
+__device__ __forceinline__ void dma16(const void *gsrc, u32x4 *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 

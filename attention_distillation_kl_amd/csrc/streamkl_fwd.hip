@@ -104,47 +104,37 @@ void fwd_kernel(FwdParams p) {
 
   const char *kb1 = p.k1 + koff;
   const char *kb2 = p.k2 + koff;
-  u32x4 st1[C::kLoads], st2[C::kLoads];
 
-  auto gload = [&](int kt) {
+  // Stage key tile kt into LDS buffer `stage` with direct global->LDS copies.
+  // Lane L of wave w fills chunk position p = i*256 + 64w + L of the tile;
+  // the global side picks the (row, logical chunk) that belongs there under
+  // the XOR swizzle (which is its own inverse).  Rows past N_K repeat the
+  // last key; the compute masks them.
+  auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int u = tid + i * C::kThreads;
-      const int row = u / G::kChunks, ch = u % G::kChunks;
-      const int key = kt * C::kBK + row;
-      if (key < p.nk) {
-        st1[i] = *reinterpret_cast<const u32x4 *>(kb1 + size_t(key) * G::kRowBytes + ch * 16);
-        st2[i] = *reinterpret_cast<const u32x4 *>(kb2 + size_t(key) * G::kRowBytes + ch * 16);
-      } else {
-        st1[i] = st2[i] = zero4();
-      }
-    }
-  };
-  auto swrite = [&](int stage) {
-    u32x4 *b1 = lds + (stage * 2 + 0) * C::kTileChunks;
-    u32x4 *b2 = lds + (stage * 2 + 1) * C::kTileChunks;
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int u = tid + i * C::kThreads;
-      const int row = u / G::kChunks, ch = u % G::kChunks;
-      const int pos = row * G::kChunks + swz<G::kChunks>(row, ch);
-      b1[pos] = st1[i];
-      b2[pos] = st2[i];
+      const int pos = i * C::kThreads + tid;
+      const int row = pos / G::kChunks;
+      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+      const int key = min(kt * C::kBK + row, p.nk - 1);
+      const size_t o = size_t(key) * G::kRowBytes + ch * 16;
+      u32x4 *w1 = lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64;
+      u32x4 *w2 = lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64;
+      dma16(kb1 + o, w1);
+      dma16(kb2 + o, w2);
     }
   };
 
   const float c = p.c;
   float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f, acc = 0.f;
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
+  if (ntiles > 0) issue(0, 0);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+    // Buffer stage^1 was last read in iteration kt-1, which ended in a barrier.
+    if (kt + 1 < ntiles) issue(kt + 1, stage ^ 1);
     const int kbase = kt * C::kBK;
 
     if (wave_active && kbase <= w_hi) {
@@ -166,14 +156,14 @@ void fwd_kernel(FwdParams p) {
 
       // Does any element of this tile lie past some row's last key?
       const bool need_mask = kbase + C::kBK - 1 > w_lo;
-      float tm1 = -INFINITY, tm2 = -INFINITY;
+      float tm1 = m1, tm2 = m2;
       if (!need_mask) {
 #pragma unroll
         for (int sb = 0; sb < C::kSub; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
-            tm1 = fmaxf(tm1, fmaxf(s1[sb][r], s1[sb][r + 1]));
-            tm2 = fmaxf(tm2, fmaxf(s2[sb][r], s2[sb][r + 1]));
+            tm1 = vmax3(s1[sb][r], s1[sb][r + 1], tm1);
+            tm2 = vmax3(s2[sb][r], s2[sb][r + 1], tm2);
           }
       } else {
 #pragma unroll
@@ -181,11 +171,11 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const bool ok = kbase + sb * 32 + c_row(r, h) <= my_last;
-            tm1 = fmaxf(tm1, ok ? s1[sb][r] : -INFINITY);
-            tm2 = fmaxf(tm2, ok ? s2[sb][r] : -INFINITY);
+            tm1 = vmax(tm1, ok ? s1[sb][r] : -INFINITY);
+            tm2 = vmax(tm2, ok ? s2[sb][r] : -INFINITY);
           }
       }
-      const float m1n = fmaxf(m1, tm1), m2n = fmaxf(m2, tm2);
+      const float m1n = tm1, m2n = tm2;
       const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - m1n) * c);
       const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - m2n) * c);
       const float nm1c = -m1n * c, nm2c = -m2n * c;
@@ -229,15 +219,14 @@ void fwd_kernel(FwdParams p) {
       m2 = m2n;
     }
 
-    if (kt + 1 < ntiles) swrite(stage ^ 1);
-    __syncthreads();
+    __syncthreads();  // also waits for the copies into stage^1
   }
 
   // Merge the two lane-halves (disjoint key subsets of the same query).
   const float om1 = __shfl_xor(m1, 32), om2 = __shfl_xor(m2, 32);
   const float ol1 = __shfl_xor(l1, 32), ol2 = __shfl_xor(l2, 32);
   const float oacc = __shfl_xor(acc, 32);
-  const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+  const float M1 = vmax(m1, om1), M2 = vmax(m2, om2);
   const float fa1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - M1) * c);
   const float fb1 = (om1 == -INFINITY) ? 0.f : fast_exp2((om1 - M1) * c);
   const float fa2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - M2) * c);

@@ -37,7 +37,21 @@ def parse():
                     help="skip timing the CPU oracle (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
+    WRITE_SIZE readings of the StreamKL kernels to bytes."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, q1, k1, q2, k2, target_s):
@@ -68,6 +82,9 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the per-head work is independent and would shard over heads with no exchange)",
