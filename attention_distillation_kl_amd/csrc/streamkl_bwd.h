@@ -47,6 +47,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace streamkl {
 
@@ -79,24 +80,49 @@ struct BwdParams {
   float inv_scale;
 };
 
-// Per-row constants: L_t = LSE_t log2(e) (P_t = exp2(s_t c - L_t)), the
-// upstream gradient g (1 without one), dp = delta / scale and gd = g dp.
-// Rows past N_Q get L = +inf and zeros, so every product they enter is zero.
+// Per-row constants of the recompute.
+//  ROLE_DQ (the lane's own query, in registers): L_t = LSE_t log2(e) so that
+//    P_t = exp2(s_t c - L_t); g (1 without an upstream gradient);
+//    dp = delta / scale with delta = KL + LSE1 - LSE2.
+//  ROLE_DK (streamed queries, in LDS): cs_t = -LSE_t / scale, used as the
+//    initial accumulator of the score products so they yield
+//    s_t' = s_t - LSE_t / scale and P_t = exp2(s_t' c); then
+//    s1 - s2 - delta/scale = s1' - s2' - KL/scale, so the only per-element
+//    constant left is gk = g KL / scale (and g itself when g varies).
+// Rows past N_Q get neutral values that make every product they enter zero.
 struct RowCst {
-  float l1, l2, g, gd, dp;
+  float l1, l2, g, dp;      // ROLE_DQ
+  float cs1, cs2, gk;       // ROLE_DK
 };
 
 __device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bool valid) {
-  RowCst r{INFINITY, INFINITY, 0.f, 0.f, 0.f};
+  // -1e30 (not -inf) keeps s1' - s2' finite (0) on rows past the end.
+  RowCst r{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};
   if (valid) {
-    const float lse1 = p.lse1[i], lse2 = p.lse2[i];
-    r.dp = (p.kl[i] + lse1 - lse2) * p.inv_scale;
+    const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
     r.g = p.dkl ? p.dkl[i] : 1.f;
     r.l1 = lse1 * kLog2e;
     r.l2 = lse2 * kLog2e;
-    r.gd = r.g * r.dp;
+    r.dp = (kl + lse1 - lse2) * p.inv_scale;
+    r.cs1 = -lse1 * p.inv_scale;
+    r.cs2 = -lse2 * p.inv_scale;
+    r.gk = r.g * kl * p.inv_scale;
   }
   return r;
+}
+
+// Scheduling template for a region that mixes matrix-core products with
+// independent VALU work: kMfma times {kDs LDS reads, 1 MFMA, 10 VALU}.  It
+// keeps operand reads close to their product (bounding register pressure)
+// and spreads the VALU stream between products so both pipes stay busy.
+template <int kMfma, int kDs>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU
+  }
 }
 
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
@@ -149,7 +175,7 @@ void bwd_kernel(BwdParams p) {
   }
 
   // ROLE_DQ: the lane's query is stationary; its constants live in registers.
-  RowCst rc{INFINITY, INFINITY, 0.f, 0.f, 0.f};
+  RowCst rc{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};
   if (ROLE == ROLE_DQ) rc = row_constants(p, size_t(bh) * p.nq + srow, srow < p.nq);
 
   // Streamed range and per-element admissibility.
@@ -193,7 +219,7 @@ void bwd_kernel(BwdParams p) {
       dma16(Y2 + o, base + C::kOffY2);
     }
   };
-  RowCst nc{INFINITY, INFINITY, 0.f, 0.f, 0.f};  // ROLE_DK: next tile's row constants
+  RowCst nc{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};  // ROLE_DK: next tile's row constants
   auto cload = [&](int tile) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
       const int row = tile * C::kBT + tid;
@@ -203,10 +229,10 @@ void bwd_kernel(BwdParams p) {
   auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
       float *cst = reinterpret_cast<float *>(lds + stage * C::kStage + C::kOffCst);
-      cst[tid] = nc.l1;
-      cst[C::kBT + tid] = nc.l2;
+      cst[tid] = nc.cs1;
+      cst[C::kBT + tid] = nc.cs2;
       cst[2 * C::kBT + tid] = nc.g;
-      cst[3 * C::kBT + tid] = nc.gd;
+      cst[3 * C::kBT + tid] = nc.gk;
     }
   };
 
@@ -226,9 +252,22 @@ void bwd_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One streamed tile.  `stage_c` is the LDS buffer as a compile-time
+  // constant, so every LDS address below is a loop-invariant lane offset plus
+  // an immediate; the loop is unrolled by two to alternate the buffers.
+  // e1/e2 of one 32-row block in the form the gradient product consumes:
+  // packed bf16 B operands for the two 16-row k-steps, or fp32 values.
+  struct EBlock {
+    u32x4 pk1[2], pk2[2];
+    float e1[16], e2[16];
+  };
+
+  // One streamed tile.  `stage_c` is the LDS buffer as a compile-time
+  // constant, so every LDS address below is a loop-invariant lane offset plus
+  // an immediate; the loop is unrolled by two to alternate the buffers.
+  auto tile_step = [&](int it, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const int tile = tile0 + it;
-    const int stage = it & 1;
     // Buffer stage^1 was last read in iteration it-1, which ended in a barrier.
     if (it + 1 < ntiles) {
       issue(tile + 1, stage ^ 1);
@@ -237,14 +276,25 @@ void bwd_kernel(BwdParams p) {
     const u32x4 *ybase = lds + stage * C::kStage;
     const float *cst = reinterpret_cast<const float *>(ybase + C::kOffCst);
 
+    // 1. recompute the two score blocks of block sb
+    auto scores = [&](int sb, f32x16 &s1, f32x16 &s2) {
+      if (ROLE == ROLE_DK) {
+        // initial accumulators -LSE_t/scale of the block's rows, in C layout
 #pragma unroll
-    for (int sb = 0; sb < C::kSub; ++sb) {
-      const int tb = tile * C::kBT + sb * 32;  // first streamed row of this block
-      const bool live = ROLE == ROLE_DQ ? tb <= w_any : tb + 31 >= w_any;
-      if (!(wave_active && live)) continue;
-
-      // 1. recompute the two score blocks
-      f32x16 s1 = f32x16{}, s2 = f32x16{};
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = sb * 32 + g4 * 8 + 4 * h;
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(cst + r0);
+          const f32x4 v2 = *reinterpret_cast<const f32x4 *>(cst + C::kBT + r0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s1[4 * g4 + q] = v1[q];
+            s2[4 * g4 + q] = v2[q];
+          }
+        }
+      } else {
+        s1 = f32x16{};
+        s2 = f32x16{};
+      }
       const int arow = sb * 32 + col;
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
@@ -252,58 +302,67 @@ void bwd_kernel(BwdParams p) {
         mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
         mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
       }
+    };
 
-      // 2. regenerate P and form e1, e2 (fp32)
-      bool need_mask;
-      if (ROLE == ROLE_DQ) need_mask = tb + 31 > w_easy;
-      else need_mask = (CAUSAL && tb < w_easy) || tb + 32 > p.nq;
-      float e1[16], e2[16];
+    // 2. regenerate P and form e1, e2 (fp32); the admissibility mask is
+    //    applied only on blocks that straddle a frontier or the end.
+    auto form = [&](int sb, const f32x16 &s1, const f32x16 &s2, EBlock &E, auto masked_c) {
+      constexpr bool kMasked = decltype(masked_c)::value;
+      const int tb = tile * C::kBT + sb * 32;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 L1v, L2v, Gv, GDv;
+        f32x4 Gv, GKv;
         if (ROLE == ROLE_DK) {
           const int r0 = sb * 32 + g4 * 8 + 4 * h;
-          L1v = *reinterpret_cast<const f32x4 *>(cst + r0);
-          L2v = *reinterpret_cast<const f32x4 *>(cst + C::kBT + r0);
           if (GSIGN) Gv = *reinterpret_cast<const f32x4 *>(cst + 2 * C::kBT + r0);
-          GDv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
+          GKv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = g4 * 4 + q;
-          const float L1 = ROLE == ROLE_DK ? L1v[q] : rc.l1;
-          const float L2 = ROLE == ROLE_DK ? L2v[q] : rc.l2;
-          // ROLE_DK: g dp of the streamed row (dp itself when there is no g);
-          // ROLE_DQ: dp of the lane's own row, g is applied at write-out.
-          const float gd = ROLE == ROLE_DK ? GDv[q] : rc.dp;
-          float p1 = fast_exp2(fmaf(s1[r], c, -L1));
-          float p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -L2)) : 0.f;
-          if (need_mask) {
+          float p1, p2;
+          if (ROLE == ROLE_DK) {  // s_t already carry -LSE_t/scale
+            p1 = fast_exp2(s1[r] * c);
+            p2 = kG2 ? fast_exp2(s2[r] * c) : 0.f;
+          } else {
+            p1 = fast_exp2(fmaf(s1[r], c, -rc.l1));
+            p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -rc.l2)) : 0.f;
+          }
+          if constexpr (kMasked) {
             const int tau = tb + c_row(r, h);
             const bool ok = ROLE == ROLE_DQ ? tau <= lim : (tau >= lim && tau < p.nq);
             p1 = ok ? p1 : 0.f;
             p2 = ok ? p2 : 0.f;
           }
           if (ROLE == ROLE_DK && GSIGN) {
-            e2[r] = (p2 - p1) * Gv[q];
-            e1[r] = p1 * fmaf(s1[r] - s2[r], Gv[q], -gd);
+            E.e2[r] = (p2 - p1) * Gv[q];
+            E.e1[r] = p1 * fmaf(s1[r] - s2[r], Gv[q], -GKv[q]);
+          } else if (ROLE == ROLE_DK) {
+            E.e2[r] = p2 - p1;
+            E.e1[r] = p1 * ((s1[r] - s2[r]) - GKv[q]);
           } else {
-            e2[r] = p2 - p1;
-            e1[r] = p1 * ((s1[r] - s2[r]) - gd);
+            // ROLE_DQ: dp of the lane's own row; g is applied at write-out.
+            E.e2[r] = p2 - p1;
+            E.e1[r] = p1 * ((s1[r] - s2[r]) - rc.dp);
           }
         }
       }
+      if constexpr (BF16) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            E.pk1[ks][w] = pack_bf16(E.e1[8 * ks + 2 * w], E.e1[8 * ks + 2 * w + 1]);
+            E.pk2[ks][w] = pack_bf16(E.e2[8 * ks + 2 * w], E.e2[8 * ks + 2 * w + 1]);
+          }
+      }
+    };
 
-      // 3. gradient products: dX_t^T += Y_t^T e_t
+    // 3. gradient products of block sb: dX_t^T += Y_t^T e_t
+    auto grad = [&](int sb, const EBlock &E) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if constexpr (BF16) {
-          u32x4 b1, b2;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            b1[w] = pack_bf16(e1[8 * ks + 2 * w], e1[8 * ks + 2 * w + 1]);
-            b2[w] = pack_bf16(e2[8 * ks + 2 * w], e2[8 * ks + 2 * w + 1]);
-          }
           // transposing-read supplier: row sb*32 + 16ks + 8t + 4h + s/4,
           // columns mb*32 + 16(grp&1) + 4(s&3) .. +3   (s = lane % 16, grp = lane / 16)
           const int s16 = lane & 15, grp = lane >> 4;
@@ -328,10 +387,10 @@ void bwd_kernel(BwdParams p) {
             }
             if (kG1)
               acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1), acc1[mb], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, E.pk1[ks]), acc1[mb], 0, 0, 0);
             if (kG2)
               acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b2), acc2[mb], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, E.pk2[ks]), acc2[mb], 0, 0, 0);
           }
         } else {
           const float *yf1 = reinterpret_cast<const float *>(ybase);
@@ -343,16 +402,63 @@ void bwd_kernel(BwdParams p) {
             for (int j = 0; j < 8; ++j) {
               const int row = sb * 32 + 16 * ks + c_row(j, h);
               const int idx = (row * G::kChunks + swz<G::kChunks>(row, d >> 2)) * 4 + (d & 3);
-              if (kG1) acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf1[idx], e1[8 * ks + j], acc1[mb], 0, 0, 0);
-              if (kG2) acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf2[idx], e2[8 * ks + j], acc2[mb], 0, 0, 0);
+              if (kG1) acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf1[idx], E.e1[8 * ks + j], acc1[mb], 0, 0, 0);
+              if (kG2) acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf2[idx], E.e2[8 * ks + j], acc2[mb], 0, 0, 0);
             }
           }
         }
+      }
+    };
+
+    // Per block: is any of the wave's elements admissible (live), and does
+    // any element need the mask?
+    auto live_at = [&](int tb) { return wave_active && (ROLE == ROLE_DQ ? tb <= w_any : tb + 31 >= w_any); };
+    auto mask_at = [&](int tb) {
+      return ROLE == ROLE_DQ ? tb + 31 > w_easy : ((CAUSAL && tb < w_easy) || tb + 32 > p.nq);
+    };
+    const int tb0 = tile * C::kBT;
+    bool plain = true;
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) plain = plain && live_at(tb0 + 32 * sb) && !mask_at(tb0 + 32 * sb);
+
+    if (C::kSub == 2 && plain) {
+      // Interior tile, software-pipelined over its two blocks so each phase
+      // pairs matrix-core work with independent VALU work:
+      //   scores(0) | scores(1) + form(0) | grad(0) + form(1) | grad(1)
+      f32x16 sa1, sa2, sb1, sb2;
+      EBlock Ea, Eb;
+      scores(0, sa1, sa2);
+      __builtin_amdgcn_sched_barrier(0);
+      scores(1, sb1, sb2);
+      form(0, sa1, sa2, Ea, std::false_type{});
+      interleave<2 * G::kLaneChunks, 1>();
+      __builtin_amdgcn_sched_barrier(0);
+      grad(0, Ea);
+      form(1, sb1, sb2, Eb, std::false_type{});
+      interleave<(kG1 + kG2) * 2 * kMB, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      grad(1, Eb);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < C::kSub; ++sb) {
+        const int tb = tb0 + sb * 32;
+        if (!live_at(tb)) continue;
+        f32x16 s1, s2;
+        EBlock E;
+        scores(sb, s1, s2);
+        if (mask_at(tb)) form(sb, s1, s2, E, std::true_type{});
+        else form(sb, s1, s2, E, std::false_type{});
+        grad(sb, E);
       }
     }
 
     if (it + 1 < ntiles) cstore(stage ^ 1);
     __syncthreads();  // also waits for the copies into stage^1
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---------------------------------------------------------------- write-out

@@ -13,8 +13,10 @@
 // Key tiles past a query block's causal frontier are never visited.
 //
 // Mapping to the hardware:
-//   * one workgroup = 4 waves x 32 query rows; each wave keeps its queries'
-//     Q1/Q2 fragments in registers for the whole key loop;
+//   * one workgroup = 4 waves x 64 query rows (32 for fp32 with d = 128);
+//     each wave keeps its queries' Q1/Q2 fragments in registers for the
+//     whole key loop, and every K fragment it reads from LDS feeds the
+//     products of both of its 32-query blocks;
 //   * K1/K2 tiles (64 keys for bf16, 32 for fp32) are staged in LDS, double
 //     buffered through registers, with an XOR chunk swizzle;
 //   * scores are computed transposed (S^T = K Q^T, 32x32 MFMA blocks) so each
@@ -28,6 +30,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace streamkl {
 namespace {
@@ -37,11 +40,13 @@ struct FwdCfg {
   using G = RowGeom<BF16, D>;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBQ = 32 * kWaves;                 // queries per workgroup
+  static constexpr int kNQB = (BF16 || D == 64) ? 2 : 1;  // 32-query blocks per wave
+  static constexpr int kWQ = 32 * kNQB;                   // queries per wave
+  static constexpr int kBQ = kWQ * kWaves;                // queries per workgroup
   static constexpr int kBK = BF16 ? 64 : 32;              // keys per LDS tile
   static constexpr int kSub = kBK / 32;                   // 32-key blocks per tile
   static constexpr int kTileChunks = kBK * G::kChunks;    // 16-B chunks per tensor tile
-  static constexpr int kLoads = kTileChunks / kThreads;   // chunks per thread per tensor
+  static constexpr int kLoads = kTileChunks / kThreads;   // copies per thread per tensor
   static constexpr size_t kLdsBytes = size_t(2) * 2 * kTileChunks * 16;  // 2 stages x K1,K2
   static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
 };
@@ -58,6 +63,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void fwd_kernel(FwdParams p) {
   using C = FwdCfg<BF16, D>;
   using G = typename C::G;
+  constexpr int NQB = C::kNQB;
   extern __shared__ u32x4 lds[];  // [stage][tensor][kTileChunks]
 
   const int tid = threadIdx.x;
@@ -71,26 +77,29 @@ void fwd_kernel(FwdParams p) {
   const int qbr = bid - bh * p.nqb;
   const int qb = CAUSAL ? p.nqb - 1 - qbr : qbr;
   const int q0 = qb * C::kBQ;
-  const int wq0 = q0 + wave * 32;
-  const int qrow = wq0 + col;
+  const int wq0 = q0 + wave * C::kWQ;
   const bool wave_active = wq0 < p.nq;
 
   const size_t qoff = size_t(bh) * p.nq * G::kRowBytes;
   const size_t koff = size_t(bh) * p.nk * G::kRowBytes;
 
   // Stationary query fragments (B operand), zero for rows past N_Q.
-  u32x4 qf1[G::kLaneChunks], qf2[G::kLaneChunks];
-  if (qrow < p.nq) {
-    const u32x4 *r1 = reinterpret_cast<const u32x4 *>(p.q1 + qoff + size_t(qrow) * G::kRowBytes);
-    const u32x4 *r2 = reinterpret_cast<const u32x4 *>(p.q2 + qoff + size_t(qrow) * G::kRowBytes);
+  u32x4 qf1[NQB][G::kLaneChunks], qf2[NQB][G::kLaneChunks];
 #pragma unroll
-    for (int c = 0; c < G::kLaneChunks; ++c) {
-      qf1[c] = r1[frag_chunk<BF16, D>(h, c)];
-      qf2[c] = r2[frag_chunk<BF16, D>(h, c)];
+  for (int j = 0; j < NQB; ++j) {
+    const int qrow = wq0 + 32 * j + col;
+    if (qrow < p.nq) {
+      const u32x4 *r1 = reinterpret_cast<const u32x4 *>(p.q1 + qoff + size_t(qrow) * G::kRowBytes);
+      const u32x4 *r2 = reinterpret_cast<const u32x4 *>(p.q2 + qoff + size_t(qrow) * G::kRowBytes);
+#pragma unroll
+      for (int c = 0; c < G::kLaneChunks; ++c) {
+        qf1[j][c] = r1[frag_chunk<BF16, D>(h, c)];
+        qf2[j][c] = r2[frag_chunk<BF16, D>(h, c)];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < G::kLaneChunks; ++c) qf1[j][c] = qf2[j][c] = zero4();
     }
-  } else {
-#pragma unroll
-    for (int c = 0; c < G::kLaneChunks; ++c) qf1[c] = qf2[c] = zero4();
   }
 
   // Key range: [0, kend).  Causal: the last allowed key of row i is i + N_K - N_Q.
@@ -98,18 +107,26 @@ void fwd_kernel(FwdParams p) {
   int kend = p.nk;
   if (CAUSAL) kend = min(p.nk, min(q0 + C::kBQ, p.nq) + off);
   const int ntiles = (kend + C::kBK - 1) / C::kBK;
-  const int my_last = CAUSAL ? min(qrow + off, p.nk - 1) : p.nk - 1;
-  const int w_lo = CAUSAL ? min(wq0 + off, p.nk - 1) : p.nk - 1;       // smallest in the wave
-  const int w_hi = CAUSAL ? min(wq0 + 31 + off, p.nk - 1) : p.nk - 1;  // largest in the wave
+  // Per 32-query block j of the wave: the lane's last key, and the smallest
+  // and largest last key over the block (wave-uniform).
+  int my_last[NQB], blk_lo[NQB], blk_hi[NQB];
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const int r0 = wq0 + 32 * j;
+    my_last[j] = CAUSAL ? min(r0 + col + off, p.nk - 1) : p.nk - 1;
+    blk_lo[j] = CAUSAL ? min(r0 + off, p.nk - 1) : p.nk - 1;
+    blk_hi[j] = CAUSAL ? min(r0 + 31 + off, p.nk - 1) : p.nk - 1;
+  }
+  const int w_hi = blk_hi[NQB - 1];
 
   const char *kb1 = p.k1 + koff;
   const char *kb2 = p.k2 + koff;
 
   // Stage key tile kt into LDS buffer `stage` with direct global->LDS copies.
-  // Lane L of wave w fills chunk position p = i*256 + 64w + L of the tile;
-  // the global side picks the (row, logical chunk) that belongs there under
-  // the XOR swizzle (which is its own inverse).  Rows past N_K repeat the
-  // last key; the compute masks them.
+  // Lane L of wave w fills chunk position i*256 + 64w + L of the tile; the
+  // global side picks the (row, logical chunk) that belongs there under the
+  // XOR swizzle (its own inverse).  Rows past N_K repeat the last key; the
+  // compute masks them.
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
@@ -126,7 +143,69 @@ void fwd_kernel(FwdParams p) {
   };
 
   const float c = p.c;
-  float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  // The five running scalars per query block and lane-half.
+  float m1[NQB], m2[NQB], l1[NQB], l2[NQB], acc[NQB];
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    m1[j] = m2[j] = -INFINITY;
+    l1[j] = l2[j] = acc[j] = 0.f;
+  }
+
+  // Online update of query block j's scalars with one 32-key block of scores.
+  auto fold = [&](int j, const f32x16 &s1, const f32x16 &s2, int kb, auto masked_c) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    float ta1 = m1[j], tb1 = m1[j], ta2 = m2[j], tb2 = m2[j];
+    if constexpr (!kMasked) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        ta1 = vmax3(s1[r], s1[r + 1], ta1);
+        tb1 = vmax3(s1[r + 2], s1[r + 3], tb1);
+        ta2 = vmax3(s2[r], s2[r + 1], ta2);
+        tb2 = vmax3(s2[r + 2], s2[r + 3], tb2);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const bool oka = kb + c_row(r, h) <= my_last[j];
+        const bool okb = kb + c_row(r + 1, h) <= my_last[j];
+        ta1 = vmax(ta1, oka ? s1[r] : -INFINITY);
+        tb1 = vmax(tb1, okb ? s1[r + 1] : -INFINITY);
+        ta2 = vmax(ta2, oka ? s2[r] : -INFINITY);
+        tb2 = vmax(tb2, okb ? s2[r + 1] : -INFINITY);
+      }
+    }
+    const float tm1 = vmax(ta1, tb1), tm2 = vmax(ta2, tb2);
+    const float a1 = (m1[j] == -INFINITY) ? 0.f : fast_exp2((m1[j] - tm1) * c);
+    const float a2 = (m2[j] == -INFINITY) ? 0.f : fast_exp2((m2[j] - tm2) * c);
+    const float nm1c = -tm1 * c, nm2c = -tm2 * c;
+    float ts1a = 0.f, ts1b = 0.f, ts2a = 0.f, ts2b = 0.f, tda = 0.f, tdb = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p1a = fast_exp2(fmaf(s1[r], c, nm1c));
+      float p2a = fast_exp2(fmaf(s2[r], c, nm2c));
+      float p1b = fast_exp2(fmaf(s1[r + 1], c, nm1c));
+      float p2b = fast_exp2(fmaf(s2[r + 1], c, nm2c));
+      if constexpr (kMasked) {
+        const bool oka = kb + c_row(r, h) <= my_last[j];
+        const bool okb = kb + c_row(r + 1, h) <= my_last[j];
+        p1a = oka ? p1a : 0.f;
+        p2a = oka ? p2a : 0.f;
+        p1b = okb ? p1b : 0.f;
+        p2b = okb ? p2b : 0.f;
+      }
+      ts1a += p1a;
+      ts2a += p2a;
+      ts1b += p1b;
+      ts2b += p2b;
+      tda = fmaf(p1a, s1[r] - s2[r], tda);
+      tdb = fmaf(p1b, s1[r + 1] - s2[r + 1], tdb);
+    }
+    l1[j] = fmaf(l1[j], a1, ts1a + ts1b);
+    l2[j] = fmaf(l2[j], a2, ts2a + ts2b);
+    acc[j] = fmaf(acc[j], a1, tda + tdb);
+    m1[j] = tm1;
+    m2[j] = tm2;
+  };
 
   if (ntiles > 0) issue(0, 0);
   __syncthreads();
@@ -135,113 +214,86 @@ void fwd_kernel(FwdParams p) {
     const int stage = kt & 1;
     // Buffer stage^1 was last read in iteration kt-1, which ended in a barrier.
     if (kt + 1 < ntiles) issue(kt + 1, stage ^ 1);
-    const int kbase = kt * C::kBK;
+    const u32x4 *b1 = lds + (stage * 2 + 0) * C::kTileChunks;
+    const u32x4 *b2 = lds + (stage * 2 + 1) * C::kTileChunks;
 
-    if (wave_active && kbase <= w_hi) {
-      const u32x4 *b1 = lds + (stage * 2 + 0) * C::kTileChunks;
-      const u32x4 *b2 = lds + (stage * 2 + 1) * C::kTileChunks;
-      f32x16 s1[C::kSub], s2[C::kSub];
 #pragma unroll
-      for (int sb = 0; sb < C::kSub; ++sb) {
-        s1[sb] = f32x16{};
-        s2[sb] = f32x16{};
-        const int row = sb * 32 + col;
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      const int kb = kt * C::kBK + sb * 32;
+      if (!wave_active || kb > w_hi) continue;  // past every row's frontier
+
+      // Scores S^T = K Q^T of this key block for all query blocks: each K
+      // fragment is read from LDS once and used for NQB products.
+      f32x16 s1[NQB], s2[NQB];
 #pragma unroll
-        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-          const int pos = row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc));
-          mfma_chunk<BF16>(b1[pos], qf1[cc], s1[sb]);
-          mfma_chunk<BF16>(b2[pos], qf2[cc], s2[sb]);
+      for (int j = 0; j < NQB; ++j) {
+        s1[j] = f32x16{};
+        s2[j] = f32x16{};
+      }
+      const int row = sb * 32 + col;
+#pragma unroll
+      for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+        const int pos = row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc));
+        const u32x4 a1 = b1[pos], a2 = b2[pos];
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) {
+          mfma_chunk<BF16>(a1, qf1[j][cc], s1[j]);
+          mfma_chunk<BF16>(a2, qf2[j][cc], s2[j]);
         }
       }
+      if constexpr (BF16) {
+        // Keep each K fragment read next to its products: reading all of them
+        // up front would need 64 more registers than a wave has.
+#pragma unroll
+        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // 2 LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);  // their products
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
-      // Does any element of this tile lie past some row's last key?
-      const bool need_mask = kbase + C::kBK - 1 > w_lo;
-      float tm1 = m1, tm2 = m2;
-      if (!need_mask) {
+      // Fold each query block: plain when the whole block is admissible.
+      bool plain = true;
 #pragma unroll
-        for (int sb = 0; sb < C::kSub; ++sb)
+      for (int j = 0; j < NQB; ++j) plain = plain && kb + 31 <= blk_lo[j];
+      if (plain) {
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            tm1 = vmax3(s1[sb][r], s1[sb][r + 1], tm1);
-            tm2 = vmax3(s2[sb][r], s2[sb][r + 1], tm2);
-          }
+        for (int j = 0; j < NQB; ++j) fold(j, s1[j], s2[j], kb, std::false_type{});
       } else {
 #pragma unroll
-        for (int sb = 0; sb < C::kSub; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool ok = kbase + sb * 32 + c_row(r, h) <= my_last;
-            tm1 = vmax(tm1, ok ? s1[sb][r] : -INFINITY);
-            tm2 = vmax(tm2, ok ? s2[sb][r] : -INFINITY);
-          }
+        for (int j = 0; j < NQB; ++j) {
+          if (kb > blk_hi[j]) continue;
+          if (kb + 31 > blk_lo[j]) fold(j, s1[j], s2[j], kb, std::true_type{});
+          else fold(j, s1[j], s2[j], kb, std::false_type{});
+        }
       }
-      const float m1n = tm1, m2n = tm2;
-      const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - m1n) * c);
-      const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - m2n) * c);
-      const float nm1c = -m1n * c, nm2c = -m2n * c;
-
-      float ts1a = 0.f, ts1b = 0.f, ts2a = 0.f, ts2b = 0.f, ta = 0.f, tb = 0.f;
-      if (!need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < C::kSub; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p1a = fast_exp2(fmaf(s1[sb][r], c, nm1c));
-            const float p2a = fast_exp2(fmaf(s2[sb][r], c, nm2c));
-            const float p1b = fast_exp2(fmaf(s1[sb][r + 1], c, nm1c));
-            const float p2b = fast_exp2(fmaf(s2[sb][r + 1], c, nm2c));
-            ts1a += p1a;
-            ts2a += p2a;
-            ts1b += p1b;
-            ts2b += p2b;
-            ta = fmaf(p1a, s1[sb][r] - s2[sb][r], ta);
-            tb = fmaf(p1b, s1[sb][r + 1] - s2[sb][r + 1], tb);
-          }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < C::kSub; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool ok = kbase + sb * 32 + c_row(r, h) <= my_last;
-            const float e1 = fast_exp2(fmaf(s1[sb][r], c, nm1c));
-            const float e2 = fast_exp2(fmaf(s2[sb][r], c, nm2c));
-            const float p1 = ok ? e1 : 0.f;
-            const float p2 = ok ? e2 : 0.f;
-            ts1a += p1;
-            ts2a += p2;
-            ta = fmaf(p1, s1[sb][r] - s2[sb][r], ta);
-          }
-      }
-      l1 = fmaf(l1, a1, ts1a + ts1b);
-      l2 = fmaf(l2, a2, ts2a + ts2b);
-      acc = fmaf(acc, a1, ta + tb);
-      m1 = m1n;
-      m2 = m2n;
     }
-
     __syncthreads();  // also waits for the copies into stage^1
   }
 
   // Merge the two lane-halves (disjoint key subsets of the same query).
-  const float om1 = __shfl_xor(m1, 32), om2 = __shfl_xor(m2, 32);
-  const float ol1 = __shfl_xor(l1, 32), ol2 = __shfl_xor(l2, 32);
-  const float oacc = __shfl_xor(acc, 32);
-  const float M1 = vmax(m1, om1), M2 = vmax(m2, om2);
-  const float fa1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - M1) * c);
-  const float fb1 = (om1 == -INFINITY) ? 0.f : fast_exp2((om1 - M1) * c);
-  const float fa2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - M2) * c);
-  const float fb2 = (om2 == -INFINITY) ? 0.f : fast_exp2((om2 - M2) * c);
-  const float L1 = l1 * fa1 + ol1 * fb1;
-  const float L2 = l2 * fa2 + ol2 * fb2;
-  const float A = acc * fa1 + oacc * fb1;
-
-  if (h == 0 && qrow < p.nq) {
-    const float lse1 = M1 * p.scale + logf(L1);
-    const float lse2 = M2 * p.scale + logf(L2);
-    const size_t o = size_t(bh) * p.nq + qrow;
-    p.kl[o] = p.scale * (A / L1) + lse2 - lse1;
-    p.lse1[o] = lse1;
-    p.lse2[o] = lse2;
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const float om1 = __shfl_xor(m1[j], 32), om2 = __shfl_xor(m2[j], 32);
+    const float ol1 = __shfl_xor(l1[j], 32), ol2 = __shfl_xor(l2[j], 32);
+    const float oacc = __shfl_xor(acc[j], 32);
+    const float M1 = vmax(m1[j], om1), M2 = vmax(m2[j], om2);
+    const float fa1 = (m1[j] == -INFINITY) ? 0.f : fast_exp2((m1[j] - M1) * c);
+    const float fb1 = (om1 == -INFINITY) ? 0.f : fast_exp2((om1 - M1) * c);
+    const float fa2 = (m2[j] == -INFINITY) ? 0.f : fast_exp2((m2[j] - M2) * c);
+    const float fb2 = (om2 == -INFINITY) ? 0.f : fast_exp2((om2 - M2) * c);
+    const float L1 = l1[j] * fa1 + ol1 * fb1;
+    const float L2 = l2[j] * fa2 + ol2 * fb2;
+    const float A = acc[j] * fa1 + oacc * fb1;
+    const int qrow = wq0 + 32 * j + col;
+    if (h == 0 && qrow < p.nq) {
+      const float lse1 = M1 * p.scale + logf(L1);
+      const float lse2 = M2 * p.scale + logf(L2);
+      const size_t o = size_t(bh) * p.nq + qrow;
+      p.kl[o] = p.scale * (A / L1) + lse2 - lse1;
+      p.lse1[o] = lse1;
+      p.lse2[o] = lse2;
+    }
   }
 }
 
