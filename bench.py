@@ -22,6 +22,39 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3
 
+CSRC = os.path.join(ROOT, "attention_distillation_kl_amd", "csrc")
+# Sources of each kernel's translation unit: the traffic counters recorded in
+# profiles/ are reported only while these hash to the recorded value.
+KERNEL_SOURCES = {
+    "fwd": ["streamkl_fwd.hip", "streamkl_device.h", "streamkl_launch.h"],
+    "bwd_dk": ["streamkl_bwd.h", "streamkl_bwd_dk.hip", "streamkl_device.h", "streamkl_launch.h"],
+    "bwd_dq": ["streamkl_bwd.h", "streamkl_bwd_dq.hip", "streamkl_device.h", "streamkl_launch.h"],
+}
+
+
+def kernel_hash(kernel):
+    import hashlib
+    m = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from profiles/<workload>_traffic.md (rocprofv3
+    FETCH_SIZE/WRITE_SIZE, copy-calibrated), or None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    want = kernel_hash(kernel)
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == want:
+                return float(parts[3])
+    return None
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -35,7 +68,7 @@ def parse():
     ap.add_argument("--workload", default="h32k")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (for profiler runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates HBM byte counters)")
@@ -71,10 +104,12 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s):
         keys = np.array([min(w.NK, i + off + 1) if w.causal else w.NK for i in range(rb, w.NQ)], dtype=np.float64)
         return dt, 16.0 * w.d * keys.sum()
 
-    probe = 16
-    dt, _ = run(probe)
-    rows = int(max(probe, min(w.NQ, probe * target_s / max(dt, 1e-3))))
-    dt, flops = run(rows)
+    rows, dt, flops = 64, 0.0, 0.0
+    for _ in range(4):  # grow the sample until it takes at least half the target time
+        dt, flops = run(rows)
+        if dt >= 0.5 * target_s or rows >= w.NQ:
+            break
+        rows = int(min(w.NQ, rows * max(2.0, target_s / max(dt, 1e-3))))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"fp64 oracle, forward+backward of the last {rows} query rows of head 0 "
                       f"({flops / 1e12:.3f} TFLOP credited, {dt:.1f} s)"}
@@ -157,7 +192,7 @@ def main():
     dom = max(kern, key=kern.get)
     ach = per_launch[dom] / (kern[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(ach / peak, 4), "traffic": None,
+            "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, dom),
             "flops_per_launch": per_launch[dom], "avg_launch_ms": round(kern[dom], 4)}
 
     cpu = None
