@@ -56,19 +56,34 @@ enum { ROLE_DQ = 0, ROLE_DK = 1 };
 template <bool BF16, int D>
 struct BwdCfg {
   using G = RowGeom<BF16, D>;
-  static constexpr int kWaves = 4;
+  // Two waves per SIMD need a wave to fit in 256 registers, so the teacher's
+  // stationary fragments live in LDS (one tile per workgroup, loaded once)
+  // and only the student's stay in registers.  fp32 with d = 128 would not
+  // fit in LDS that way; it keeps both in registers at one wave per SIMD.
+  static constexpr bool kX1Lds = BF16 || D == 64;
+  static constexpr int kWaves = kX1Lds ? 8 : 4;
+  static constexpr int kWavesPerEU = kX1Lds ? 2 : 1;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBS = 32 * kWaves;                 // stationary rows per workgroup
   static constexpr int kBT = BF16 ? 64 : 32;              // streamed rows per LDS tile
   static constexpr int kSub = kBT / 32;                   // 32-row blocks per tile
   static constexpr int kTileChunks = kBT * G::kChunks;    // 16-B chunks per tensor tile
   static constexpr int kLoads = kTileChunks / kThreads;   // copies per thread per tensor
+  static constexpr int kXChunks = kX1Lds ? kBS * G::kChunks : 0;  // stationary teacher tile
+  static constexpr int kXLoads = kXChunks / kThreads;
   static constexpr int kNCst = 4;                         // per-row constant arrays
-  static constexpr int kOffY2 = kTileChunks;
-  static constexpr int kOffCst = 2 * kTileChunks;
-  static constexpr int kStage = kOffCst + kNCst * kBT / 4;
-  static constexpr size_t kLdsBytes = size_t(2) * kStage * 16;
+  // LDS layout (16-B chunks): the row constants of both stages first, then
+  // the two stages of (Y1, Y2) tiles, then the stationary tile.  Everything a
+  // loop iteration addresses from one per-lane register stays within the
+  // 64 KiB immediate offset of the LDS instructions.
+  static constexpr int kCstStage = kNCst * kBT / 4;
+  static constexpr int kOffY = 2 * kCstStage;
+  static constexpr int kOffY2 = kTileChunks;              // within a stage
+  static constexpr int kStage = 2 * kTileChunks;
+  static constexpr int kOffX = kOffY + 2 * kStage;        // after the two stages
+  static constexpr size_t kLdsBytes = size_t(kOffX + kXChunks) * 16;
   static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  static_assert(kXChunks % kThreads == 0, "stationary tile must split evenly over the workgroup");
 };
 
 struct BwdParams {
@@ -111,22 +126,9 @@ __device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bo
   return r;
 }
 
-// Scheduling template for a region that mixes matrix-core products with
-// independent VALU work: kMfma times {kDs LDS reads, 1 MFMA, 10 VALU}.  It
-// keeps operand reads close to their product (bounding register pressure)
-// and spreads the VALU stream between products so both pipes stay busy.
-template <int kMfma, int kDs>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < kMfma; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU
-  }
-}
-
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(BwdCfg<BF16, D>::kThreads, BwdCfg<BF16, D>::kThreads),
+                          amdgpu_waves_per_eu(BwdCfg<BF16, D>::kWavesPerEU, BwdCfg<BF16, D>::kWavesPerEU)))
 void bwd_kernel(BwdParams p) {
   using C = BwdCfg<BF16, D>;
   using G = typename C::G;
@@ -158,20 +160,38 @@ void bwd_kernel(BwdParams p) {
   const int s0 = sblk * C::kBS;
   const int w0 = s0 + wave * 32;
   const int srow = w0 + col;
-  const bool wave_active = w0 < ns;
 
-  u32x4 xf1[G::kLaneChunks], xf2[G::kLaneChunks];
+  // Stationary fragments (B operand of the score products): the student's in
+  // registers; the teacher's in registers or, with kX1Lds, in the LDS tile
+  // filled below.  Rows past the end are zero (registers) or repeat the last
+  // row (LDS); neither is ever written out.
+  constexpr int kX1Regs = C::kX1Lds ? 1 : G::kLaneChunks;
+  u32x4 xf1[kX1Regs], xf2[G::kLaneChunks];
   if (srow < ns) {
     const u32x4 *r1 = reinterpret_cast<const u32x4 *>(X1 + xoff + size_t(srow) * G::kRowBytes);
     const u32x4 *r2 = reinterpret_cast<const u32x4 *>(X2 + xoff + size_t(srow) * G::kRowBytes);
 #pragma unroll
     for (int c = 0; c < G::kLaneChunks; ++c) {
-      xf1[c] = r1[frag_chunk<BF16, D>(h, c)];
+      if (!C::kX1Lds) xf1[c] = r1[frag_chunk<BF16, D>(h, c)];
       xf2[c] = r2[frag_chunk<BF16, D>(h, c)];
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < G::kLaneChunks; ++c) xf1[c] = xf2[c] = zero4();
+    for (int c = 0; c < G::kLaneChunks; ++c) {
+      if (!C::kX1Lds) xf1[c] = zero4();
+      xf2[c] = zero4();
+    }
+  }
+  if constexpr (C::kX1Lds) {
+    // the workgroup's stationary teacher rows -> LDS (swizzled like the tiles)
+#pragma unroll
+    for (int i = 0; i < C::kXLoads; ++i) {
+      const int pos = i * C::kThreads + tid;
+      const int row = pos / G::kChunks;
+      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+      const int r = min(s0 + row, ns - 1);
+      dma16(X1 + xoff + size_t(r) * G::kRowBytes + ch * 16, lds + C::kOffX + i * C::kThreads + wave * 64);
+    }
   }
 
   // ROLE_DQ: the lane's query is stationary; its constants live in registers.
@@ -188,18 +208,9 @@ void bwd_kernel(BwdParams p) {
   }
   const int tile0 = t_begin / C::kBT;
   const int tile1 = (t_end + C::kBT - 1) / C::kBT;
-  int lim;     // ROLE_DQ: last admissible key; ROLE_DK: first admissible query
-  int w_easy;  // per 32-row block: beyond this no element of the wave needs a mask
-  int w_any;   // per 32-row block: beyond this every element of the wave is masked
-  if (ROLE == ROLE_DQ) {
-    lim = CAUSAL ? min(srow + off, p.nk - 1) : p.nk - 1;
-    w_easy = CAUSAL ? min(w0 + off, p.nk - 1) : p.nk - 1;
-    w_any = CAUSAL ? min(w0 + 31 + off, p.nk - 1) : p.nk - 1;
-  } else {
-    lim = CAUSAL ? max(srow - off, 0) : 0;
-    w_easy = CAUSAL ? max(w0 + 31 - off, 0) : 0;
-    w_any = CAUSAL ? max(w0 - off, 0) : 0;
-  }
+  // ROLE_DQ: last admissible key; ROLE_DK: first admissible query.
+  const int lim = ROLE == ROLE_DQ ? (CAUSAL ? min(srow + off, p.nk - 1) : p.nk - 1)
+                                  : (CAUSAL ? max(srow - off, 0) : 0);
 
   // ------------------------------------------------------------ staging
   // Streamed tile `tile` -> LDS buffer `stage` by direct global->LDS copies.
@@ -214,7 +225,7 @@ void bwd_kernel(BwdParams p) {
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const int r = min(tile * C::kBT + row, nt - 1);
       const size_t o = size_t(r) * G::kRowBytes + ch * 16;
-      u32x4 *base = lds + stage * C::kStage + i * C::kThreads + wave * 64;
+      u32x4 *base = lds + C::kOffY + stage * C::kStage + i * C::kThreads + wave * 64;
       dma16(Y1 + o, base);
       dma16(Y2 + o, base + C::kOffY2);
     }
@@ -228,7 +239,7 @@ void bwd_kernel(BwdParams p) {
   };
   auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
-      float *cst = reinterpret_cast<float *>(lds + stage * C::kStage + C::kOffCst);
+      float *cst = reinterpret_cast<float *>(lds + stage * C::kCstStage);
       cst[tid] = nc.cs1;
       cst[C::kBT + tid] = nc.cs2;
       cst[2 * C::kBT + tid] = nc.g;
@@ -273,8 +284,8 @@ void bwd_kernel(BwdParams p) {
       issue(tile + 1, stage ^ 1);
       cload(tile + 1);
     }
-    const u32x4 *ybase = lds + stage * C::kStage;
-    const float *cst = reinterpret_cast<const float *>(ybase + C::kOffCst);
+    const u32x4 *ybase = lds + C::kOffY + stage * C::kStage;
+    const float *cst = reinterpret_cast<const float *>(lds + stage * C::kCstStage);
 
     // 1. recompute the two score blocks of block sb
     auto scores = [&](int sb, f32x16 &s1, f32x16 &s2) {
@@ -296,10 +307,17 @@ void bwd_kernel(BwdParams p) {
         s2 = f32x16{};
       }
       const int arow = sb * 32 + col;
+      const int xrow = wave * 32 + col;  // the lane's stationary row in the LDS tile
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-        const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
-        mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+        const int fc = frag_chunk<BF16, D>(h, cc);
+        const int pos = arow * G::kChunks + swz<G::kChunks>(arow, fc);
+        if constexpr (C::kX1Lds) {
+          const u32x4 x1 = lds[C::kOffX + xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
+          mfma_chunk<BF16>(ybase[pos], x1, s1);
+        } else {
+          mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+        }
         mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
       }
     };
@@ -308,7 +326,11 @@ void bwd_kernel(BwdParams p) {
     //    applied only on blocks that straddle a frontier or the end.
     auto form = [&](int sb, const f32x16 &s1, const f32x16 &s2, EBlock &E, auto masked_c) {
       constexpr bool kMasked = decltype(masked_c)::value;
-      const int tb = tile * C::kBT + sb * 32;
+      // Element r sits at streamed row tb + c_row(r, 0) + 4h: compare the
+      // compile-time part against per-lane bounds taken once per block.
+      const int rel = tile * C::kBT + sb * 32 + 4 * h;
+      const int lo = ROLE == ROLE_DQ ? INT_MIN : lim - rel;
+      const int hi = ROLE == ROLE_DQ ? lim - rel : p.nq - 1 - rel;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 Gv, GKv;
@@ -329,8 +351,8 @@ void bwd_kernel(BwdParams p) {
             p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -rc.l2)) : 0.f;
           }
           if constexpr (kMasked) {
-            const int tau = tb + c_row(r, h);
-            const bool ok = ROLE == ROLE_DQ ? tau <= lim : (tau >= lim && tau < p.nq);
+            const int cr = c_row(r, 0);  // a constant after unrolling
+            const bool ok = ROLE == ROLE_DQ ? cr <= hi : (cr >= lo && cr <= hi);
             p1 = ok ? p1 : 0.f;
             p2 = ok ? p2 : 0.f;
           }
@@ -410,46 +432,18 @@ void bwd_kernel(BwdParams p) {
       }
     };
 
-    // Per block: is any of the wave's elements admissible (live), and does
-    // any element need the mask?
-    auto live_at = [&](int tb) { return wave_active && (ROLE == ROLE_DQ ? tb <= w_any : tb + 31 >= w_any); };
-    auto mask_at = [&](int tb) {
-      return ROLE == ROLE_DQ ? tb + 31 > w_easy : ((CAUSAL && tb < w_easy) || tb + 32 > p.nq);
-    };
-    const int tb0 = tile * C::kBT;
-    bool plain = true;
+    // One straight-line path for every tile: the mask costs a compare and
+    // two selects per element, cheaper than a second copy of the loop body
+    // competing for the same 256 registers.  Blocks wholly outside the
+    // admissible region contribute exact zeros.
 #pragma unroll
-    for (int sb = 0; sb < C::kSub; ++sb) plain = plain && live_at(tb0 + 32 * sb) && !mask_at(tb0 + 32 * sb);
-
-    if (C::kSub == 2 && plain) {
-      // Interior tile, software-pipelined over its two blocks so each phase
-      // pairs matrix-core work with independent VALU work:
-      //   scores(0) | scores(1) + form(0) | grad(0) + form(1) | grad(1)
-      f32x16 sa1, sa2, sb1, sb2;
-      EBlock Ea, Eb;
-      scores(0, sa1, sa2);
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      f32x16 s1, s2;
+      EBlock E;
+      scores(sb, s1, s2);
+      form(sb, s1, s2, E, std::true_type{});
+      grad(sb, E);
       __builtin_amdgcn_sched_barrier(0);
-      scores(1, sb1, sb2);
-      form(0, sa1, sa2, Ea, std::false_type{});
-      interleave<2 * G::kLaneChunks, 1>();
-      __builtin_amdgcn_sched_barrier(0);
-      grad(0, Ea);
-      form(1, sb1, sb2, Eb, std::false_type{});
-      interleave<(kG1 + kG2) * 2 * kMB, 2>();
-      __builtin_amdgcn_sched_barrier(0);
-      grad(1, Eb);
-    } else {
-#pragma unroll
-      for (int sb = 0; sb < C::kSub; ++sb) {
-        const int tb = tb0 + sb * 32;
-        if (!live_at(tb)) continue;
-        f32x16 s1, s2;
-        EBlock E;
-        scores(sb, s1, s2);
-        if (mask_at(tb)) form(sb, s1, s2, E, std::true_type{});
-        else form(sb, s1, s2, E, std::false_type{});
-        grad(sb, E);
-      }
     }
 
     if (it + 1 < ntiles) cstore(stage ^ 1);

@@ -84,7 +84,7 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x1
 }
 
 // Row index (within a 32-row block) of accumulator register r for half h.
-__device__ __forceinline__ int c_row(int r, int h) { return (r >> 2) * 8 + 4 * h + (r & 3); }
+__host__ __device__ constexpr int c_row(int r, int h) { return (r >> 2) * 8 + 4 * h + (r & 3); }
 
 // Position of streamed row o (0..15 inside a 16-row group) in the transposed
 // LDS layout.  Lane-half h consumes positions 8h..8h+7 of a group as one run,
