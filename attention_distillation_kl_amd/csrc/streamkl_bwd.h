@@ -53,35 +53,38 @@ namespace streamkl {
 
 enum { ROLE_DQ = 0, ROLE_DK = 1 };
 
-template <bool BF16, int D>
+// PAIR (bf16, both gradients): the two waves of a pair own the same 32
+// stationary rows.  Per streamed tile each recomputes the scores of one of the
+// two 32-row blocks and forms e1, e2 there; they swap one of the two through
+// LDS, and then wave 0 accumulates the teacher's gradient and wave 1 the
+// student's over both blocks.  A wave then holds one d x 32 accumulator
+// instead of two and both stationary fragments fit in registers at two waves
+// per SIMD.
+// Otherwise (one gradient, or fp32) every wave owns its own 32 stationary rows
+// and accumulates what is asked for; the teacher's stationary fragments live
+// in an LDS tile wherever two waves per SIMD need the registers.
+template <bool BF16, int D, bool PAIR>
 struct BwdCfg {
   using G = RowGeom<BF16, D>;
-  // Two waves per SIMD need a wave to fit in 256 registers, so the teacher's
-  // stationary fragments live in LDS (one tile per workgroup, loaded once)
-  // and only the student's stay in registers.  fp32 with d = 128 would not
-  // fit in LDS that way; it keeps both in registers at one wave per SIMD.
-  static constexpr bool kX1Lds = BF16 || D == 64;
-  static constexpr int kWaves = kX1Lds ? 8 : 4;
-  static constexpr int kWavesPerEU = kX1Lds ? 2 : 1;
+  static_assert(!PAIR || BF16, "the paired layout is for bf16");
+  static constexpr bool kX1Lds = !PAIR && (BF16 || D == 64);
+  static constexpr int kWaves = (PAIR || kX1Lds) ? 8 : 4;
+  static constexpr int kWavesPerEU = (PAIR || kX1Lds) ? 2 : 1;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBS = 32 * kWaves;                 // stationary rows per workgroup
+  static constexpr int kBS = 32 * (PAIR ? kWaves / 2 : kWaves);  // stationary rows per workgroup
   static constexpr int kBT = BF16 ? 64 : 32;              // streamed rows per LDS tile
   static constexpr int kSub = kBT / 32;                   // 32-row blocks per tile
+  static_assert(!PAIR || kSub == 2, "a pair splits a tile's two blocks");
   static constexpr int kTileChunks = kBT * G::kChunks;    // 16-B chunks per tensor tile
   static constexpr int kLoads = kTileChunks / kThreads;   // copies per thread per tensor
   static constexpr int kXChunks = kX1Lds ? kBS * G::kChunks : 0;  // stationary teacher tile
   static constexpr int kXLoads = kXChunks / kThreads;
   static constexpr int kNCst = 4;                         // per-row constant arrays
-  // LDS layout (16-B chunks): the row constants of both stages first, then
-  // the two stages of (Y1, Y2) tiles, then the stationary tile.  Everything a
-  // loop iteration addresses from one per-lane register stays within the
-  // 64 KiB immediate offset of the LDS instructions.
-  static constexpr int kCstStage = kNCst * kBT / 4;
-  static constexpr int kOffY = 2 * kCstStage;
-  static constexpr int kOffY2 = kTileChunks;              // within a stage
-  static constexpr int kStage = 2 * kTileChunks;
-  static constexpr int kOffX = kOffY + 2 * kStage;        // after the two stages
-  static constexpr size_t kLdsBytes = size_t(kOffX + kXChunks) * 16;
+  static constexpr int kOffY2 = kTileChunks;              // Y2 within a stage
+  static constexpr int kStage = 2 * kTileChunks;          // one stage: (Y1, Y2) tiles
+  static constexpr size_t kLdsBytes = size_t(2 * kStage + kXChunks + (PAIR ? kWaves * 128 : 0)) * 16 +
+                                      2 * kNCst * kBT * sizeof(float);  // the kernel's static LDS
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kXChunks % kThreads == 0, "stationary tile must split evenly over the workgroup");
 };
@@ -98,48 +101,65 @@ struct BwdParams {
 // Per-row constants of the recompute.
 //  ROLE_DQ (the lane's own query, in registers): L_t = LSE_t log2(e) so that
 //    P_t = exp2(s_t c - L_t); g (1 without an upstream gradient);
-//    dp = delta / scale with delta = KL + LSE1 - LSE2.
-//  ROLE_DK (streamed queries, in LDS): cs_t = -LSE_t / scale, used as the
-//    initial accumulator of the score products so they yield
+//    dp = delta / scale with delta = KL + LSE1 - LSE2.  Rows past N_Q get
+//    L_t = inf, which makes every P they enter zero.
+//  ROLE_DK (streamed queries, in LDS per tile): cs_t = -LSE_t / scale, used as
+//    the initial accumulator of the score products so they yield
 //    s_t' = s_t - LSE_t / scale and P_t = exp2(s_t' c); then
 //    s1 - s2 - delta/scale = s1' - s2' - KL/scale, so the only per-element
 //    constant left is gk = g KL / scale (and g itself when g varies).
-// Rows past N_Q get neutral values that make every product they enter zero.
 struct RowCst {
-  float l1, l2, g, dp;      // ROLE_DQ
-  float cs1, cs2, gk;       // ROLE_DK
+  float l1, l2, g, dp;
 };
 
 __device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bool valid) {
-  // -1e30 (not -inf) keeps s1' - s2' finite (0) on rows past the end.
-  RowCst r{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};
+  RowCst r{INFINITY, INFINITY, 0.f, 0.f};
   if (valid) {
     const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
     r.g = p.dkl ? p.dkl[i] : 1.f;
     r.l1 = lse1 * kLog2e;
     r.l2 = lse2 * kLog2e;
     r.dp = (kl + lse1 - lse2) * p.inv_scale;
-    r.cs1 = -lse1 * p.inv_scale;
-    r.cs2 = -lse2 * p.inv_scale;
-    r.gk = r.g * kl * p.inv_scale;
   }
   return r;
 }
 
+// The paired layout pays off in the key-gradient role; the query-gradient
+// role is faster with one wave per 32 stationary rows.
+template <bool BF16, int MASK, int ROLE>
+constexpr bool kPairOf = BF16 && MASK == 3 && ROLE == ROLE_DK;
+
+template <bool BF16, int D, int MASK, int ROLE>
+using BwdCfgOf = BwdCfg<BF16, D, kPairOf<BF16, MASK, ROLE>>;
+
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
-__global__ __attribute__((amdgpu_flat_work_group_size(BwdCfg<BF16, D>::kThreads, BwdCfg<BF16, D>::kThreads),
-                          amdgpu_waves_per_eu(BwdCfg<BF16, D>::kWavesPerEU, BwdCfg<BF16, D>::kWavesPerEU)))
+__global__ __attribute__((amdgpu_flat_work_group_size(BwdCfgOf<BF16, D, MASK, ROLE>::kThreads,
+                                                      BwdCfgOf<BF16, D, MASK, ROLE>::kThreads),
+                          amdgpu_waves_per_eu(BwdCfgOf<BF16, D, MASK, ROLE>::kWavesPerEU,
+                                              BwdCfgOf<BF16, D, MASK, ROLE>::kWavesPerEU)))
 void bwd_kernel(BwdParams p) {
-  using C = BwdCfg<BF16, D>;
+  using C = BwdCfgOf<BF16, D, MASK, ROLE>;
   using G = typename C::G;
+  constexpr bool kPair = kPairOf<BF16, MASK, ROLE>;
   constexpr bool kG1 = (MASK & 1) != 0;
   constexpr bool kG2 = (MASK & 2) != 0;
   constexpr int kMB = D / 32;  // 32-row blocks of d in the gradient accumulators
+  // LDS, one array per role so that the compiler can tell that reading one
+  // stage (or the row constants, the stationary tile, the exchange slots)
+  // need not wait for the copies in flight into the other stage.
   extern __shared__ u32x4 lds[];
+  u32x4 *ystage0 = lds, *ystage1 = lds + C::kStage;
+  u32x4 *xtile = lds + 2 * C::kStage;
+  float (*cstage)[C::kNCst * C::kBT] = reinterpret_cast<float (*)[C::kNCst * C::kBT]>(lds + 2 * C::kStage + C::kXChunks);
+  __shared__ u32x4 xch[kPair ? C::kWaves * 128 : 1];          // pairs' exchange slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
+  // The wave's 32 stationary rows within the workgroup and, in a pair, the
+  // streamed block it scores and the gradient it accumulates (0: teacher).
+  const int wrow = kPair ? wave >> 1 : wave;
+  const int half = kPair ? wave & 1 : 0;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = bid / p.nsb;
@@ -158,7 +178,7 @@ void bwd_kernel(BwdParams p) {
   const size_t xoff = size_t(bh) * ns * G::kRowBytes;
 
   const int s0 = sblk * C::kBS;
-  const int w0 = s0 + wave * 32;
+  const int w0 = s0 + wrow * 32;
   const int srow = w0 + col;
 
   // Stationary fragments (B operand of the score products): the student's in
@@ -190,12 +210,12 @@ void bwd_kernel(BwdParams p) {
       const int row = pos / G::kChunks;
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const int r = min(s0 + row, ns - 1);
-      dma16(X1 + xoff + size_t(r) * G::kRowBytes + ch * 16, lds + C::kOffX + i * C::kThreads + wave * 64);
+      dma16(X1 + xoff + size_t(r) * G::kRowBytes + ch * 16, xtile + i * C::kThreads + wave * 64);
     }
   }
 
   // ROLE_DQ: the lane's query is stationary; its constants live in registers.
-  RowCst rc{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};
+  RowCst rc{INFINITY, INFINITY, 0.f, 0.f};
   if (ROLE == ROLE_DQ) rc = row_constants(p, size_t(bh) * p.nq + srow, srow < p.nq);
 
   // Streamed range and per-element admissibility.
@@ -225,25 +245,37 @@ void bwd_kernel(BwdParams p) {
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const int r = min(tile * C::kBT + row, nt - 1);
       const size_t o = size_t(r) * G::kRowBytes + ch * 16;
-      u32x4 *base = lds + C::kOffY + stage * C::kStage + i * C::kThreads + wave * 64;
+      u32x4 *base = (stage ? ystage1 : ystage0) + i * C::kThreads + wave * 64;
       dma16(Y1 + o, base);
       dma16(Y2 + o, base + C::kOffY2);
     }
   };
-  RowCst nc{INFINITY, INFINITY, 0.f, 0.f, -1e30f, -1e30f, 0.f};  // ROLE_DK: next tile's row constants
+  // ROLE_DK: the next tile's per-row inputs, loaded while the current tile is
+  // processed and turned into constants only at the end of the step, so the
+  // wait for these loads does not also wait for the tile copies behind them.
+  float n_lse1 = 0.f, n_lse2 = 0.f, n_kl = 0.f, n_g = 0.f;
+  bool n_ok = false;
   auto cload = [&](int tile) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
       const int row = tile * C::kBT + tid;
-      nc = row_constants(p, size_t(bh) * p.nq + row, row < p.nq);
+      n_ok = row < p.nq;
+      if (n_ok) {
+        const size_t i = size_t(bh) * p.nq + row;
+        n_lse1 = p.lse1[i];
+        n_lse2 = p.lse2[i];
+        n_kl = p.kl[i];
+        n_g = p.dkl ? p.dkl[i] : 1.f;
+      }
     }
   };
   auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
-      float *cst = reinterpret_cast<float *>(lds + stage * C::kCstStage);
-      cst[tid] = nc.cs1;
-      cst[C::kBT + tid] = nc.cs2;
-      cst[2 * C::kBT + tid] = nc.g;
-      cst[3 * C::kBT + tid] = nc.gk;
+      // Rows past N_Q: -1e30 (not -inf) keeps s1' - s2' finite (0) and P = 0.
+      float *cst = cstage[stage];
+      cst[tid] = n_ok ? -n_lse1 * p.inv_scale : -1e30f;
+      cst[C::kBT + tid] = n_ok ? -n_lse2 * p.inv_scale : -1e30f;
+      cst[2 * C::kBT + tid] = n_ok ? n_g : 0.f;
+      cst[3 * C::kBT + tid] = n_ok ? n_g * n_kl * p.inv_scale : 0.f;
     }
   };
 
@@ -257,8 +289,8 @@ void bwd_kernel(BwdParams p) {
   const float c = p.c;
   const int ntiles = tile1 - tile0;
   if (ntiles > 0) {
-    issue(tile0, 0);
     cload(tile0);
+    issue(tile0, 0);
     cstore(0);
   }
   __syncthreads();
@@ -281,11 +313,11 @@ void bwd_kernel(BwdParams p) {
     const int tile = tile0 + it;
     // Buffer stage^1 was last read in iteration it-1, which ended in a barrier.
     if (it + 1 < ntiles) {
-      issue(tile + 1, stage ^ 1);
       cload(tile + 1);
+      issue(tile + 1, stage ^ 1);
     }
-    const u32x4 *ybase = lds + C::kOffY + stage * C::kStage;
-    const float *cst = reinterpret_cast<const float *>(lds + stage * C::kCstStage);
+    const u32x4 *ybase = stage ? ystage1 : ystage0;
+    const float *cst = cstage[stage];
 
     // 1. recompute the two score blocks of block sb
     auto scores = [&](int sb, f32x16 &s1, f32x16 &s2) {
@@ -307,13 +339,13 @@ void bwd_kernel(BwdParams p) {
         s2 = f32x16{};
       }
       const int arow = sb * 32 + col;
-      const int xrow = wave * 32 + col;  // the lane's stationary row in the LDS tile
+      const int xrow = wrow * 32 + col;  // the lane's stationary row in the LDS tile
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
         const int fc = frag_chunk<BF16, D>(h, cc);
         const int pos = arow * G::kChunks + swz<G::kChunks>(arow, fc);
         if constexpr (C::kX1Lds) {
-          const u32x4 x1 = lds[C::kOffX + xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
+          const u32x4 x1 = xtile[xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
           mfma_chunk<BF16>(ybase[pos], x1, s1);
         } else {
           mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
@@ -380,43 +412,39 @@ void bwd_kernel(BwdParams p) {
       }
     };
 
-    // 3. gradient products of block sb: dX_t^T += Y_t^T e_t
-    auto grad = [&](int sb, const EBlock &E) {
+    // 3. gradient products of block sb: dX_t^T += Y_t^T e_t.
+    //    bf16: Y_t^T comes from transposing reads of the tile; lane (s, grp)
+    //    (s = lane % 16, grp = lane / 16) supplies row sb*32 + 16ks + 8t +
+    //    4h + s/4, columns mb*32 + 16(grp&1) + 4(s&3) .. +3.
+    auto grad_bf16 = [&](int sb, const char *yb, const u32x4 (&pk)[2], f32x16 (&acc)[kMB]) {
+      const int s16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (BF16) {
-          // transposing-read supplier: row sb*32 + 16ks + 8t + 4h + s/4,
-          // columns mb*32 + 16(grp&1) + 4(s&3) .. +3   (s = lane % 16, grp = lane / 16)
-          const int s16 = lane & 15, grp = lane >> 4;
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb) {
-            const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
-            u32x4 a1, a2;
+        for (int mb = 0; mb < kMB; ++mb) {
+          const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+          u32x4 a;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
-              const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
-              if (kG1) {
-                const u32x2 v = read_tr(reinterpret_cast<const char *>(ybase) + byte);
-                a1[2 * t] = v[0];
-                a1[2 * t + 1] = v[1];
-              }
-              if (kG2) {
-                const u32x2 v = read_tr(reinterpret_cast<const char *>(ybase + C::kOffY2) + byte);
-                a2[2 * t] = v[0];
-                a2[2 * t + 1] = v[1];
-              }
-            }
-            if (kG1)
-              acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, E.pk1[ks]), acc1[mb], 0, 0, 0);
-            if (kG2)
-              acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, E.pk2[ks]), acc2[mb], 0, 0, 0);
+          for (int t = 0; t < 2; ++t) {
+            const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+            const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
+            const u32x2 v = read_tr(yb + byte);
+            a[2 * t] = v[0];
+            a[2 * t + 1] = v[1];
           }
-        } else {
-          const float *yf1 = reinterpret_cast<const float *>(ybase);
-          const float *yf2 = reinterpret_cast<const float *>(ybase + C::kOffY2);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, pk[ks]), acc[mb], 0, 0, 0);
+        }
+    };
+    auto grad = [&](int sb, const EBlock &E) {
+      if constexpr (BF16) {
+        if (kG1) grad_bf16(sb, reinterpret_cast<const char *>(ybase), E.pk1, acc1);
+        if (kG2) grad_bf16(sb, reinterpret_cast<const char *>(ybase + C::kOffY2), E.pk2, acc2);
+      } else {
+        const float *yf1 = reinterpret_cast<const float *>(ybase);
+        const float *yf2 = reinterpret_cast<const float *>(ybase + C::kOffY2);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) {
             const int d = mb * 32 + col;
@@ -428,7 +456,6 @@ void bwd_kernel(BwdParams p) {
               if (kG2) acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf2[idx], E.e2[8 * ks + j], acc2[mb], 0, 0, 0);
             }
           }
-        }
       }
     };
 
@@ -436,14 +463,47 @@ void bwd_kernel(BwdParams p) {
     // two selects per element, cheaper than a second copy of the loop body
     // competing for the same 256 registers.  Blocks wholly outside the
     // admissible region contribute exact zeros.
-#pragma unroll
-    for (int sb = 0; sb < C::kSub; ++sb) {
+    if constexpr (kPair) {
       f32x16 s1, s2;
       EBlock E;
-      scores(sb, s1, s2);
-      form(sb, s1, s2, E, std::true_type{});
-      grad(sb, E);
-      __builtin_amdgcn_sched_barrier(0);
+      scores(half, s1, s2);
+      form(half, s1, s2, E, std::true_type{});
+      // Keep the operand of the gradient this wave accumulates; hand the
+      // other to the partner, which scored the other block.
+      u32x4 mine[2], theirs[2], b0[2], b1[2];
+      u32x4 *slot = xch + wave * 128 + lane;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        mine[ks] = half ? E.pk2[ks] : E.pk1[ks];
+        slot[64 * ks] = half ? E.pk1[ks] : E.pk2[ks];
+      }
+      // Barrier that waits for this wave's LDS stores only (lgkmcnt), not
+      // for the tile copies in flight; the empty asm statements keep the
+      // compiler from moving memory accesses across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const u32x4 *peer = xch + (wave ^ 1) * 128 + lane;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        theirs[ks] = peer[64 * ks];
+        b0[ks] = half ? theirs[ks] : mine[ks];
+        b1[ks] = half ? mine[ks] : theirs[ks];
+      }
+      const char *yb = reinterpret_cast<const char *>(ybase + half * C::kOffY2);
+      grad_bf16(0, yb, b0, acc1);
+      grad_bf16(1, yb, b1, acc1);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < C::kSub; ++sb) {
+        f32x16 s1, s2;
+        EBlock E;
+        scores(sb, s1, s2);
+        form(sb, s1, s2, E, std::true_type{});
+        grad(sb, E);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     if (it + 1 < ntiles) cstore(stage ^ 1);
@@ -460,36 +520,36 @@ void bwd_kernel(BwdParams p) {
   if (srow < ns) {
     const float gq = ROLE == ROLE_DQ ? rc.g : 1.f;
     const float f1 = p.scale * p.scale * gq, f2 = p.scale * gq;
-    char *O1 = ROLE == ROLE_DQ ? p.dq1 : p.dk1;
-    char *O2 = ROLE == ROLE_DQ ? p.dq2 : p.dk2;
     const size_t ro = (size_t(bh) * ns + srow) * G::kRowBytes;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t == 0 && !kG1) continue;
-      if (t == 1 && !kG2) continue;
-      char *O = (t ? O2 : O1) + ro;
-      const float f = t ? f2 : f1;
+    char *O1 = (ROLE == ROLE_DQ ? p.dq1 : p.dk1) + ro;
+    char *O2 = (ROLE == ROLE_DQ ? p.dq2 : p.dk2) + ro;
+    auto store = [&](char *O, float f, const f32x16 (&A)[kMB]) {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d0 = mb * 32 + g4 * 8 + 4 * h;
-          const f32x16 &A = t ? acc2[mb] : acc1[mb];
-          const float v0 = A[4 * g4] * f, v1 = A[4 * g4 + 1] * f;
-          const float v2 = A[4 * g4 + 2] * f, v3 = A[4 * g4 + 3] * f;
+          const float v0 = A[mb][4 * g4] * f, v1 = A[mb][4 * g4 + 1] * f;
+          const float v2 = A[mb][4 * g4 + 2] * f, v3 = A[mb][4 * g4 + 3] * f;
           if constexpr (BF16) {
             *reinterpret_cast<u32x2 *>(O + d0 * 2) = u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
           } else {
             *reinterpret_cast<f32x4 *>(O + d0 * 4) = f32x4{v0, v1, v2, v3};
           }
         }
+    };
+    if constexpr (kPair) {
+      store(half ? O2 : O1, half ? f2 : f1, acc1);
+    } else {
+      if (kG1) store(O1, f1, acc1);
+      if (kG2) store(O2, f2, acc2);
     }
   }
 }
 
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
-  using C = BwdCfg<BF16, D>;
+  using C = BwdCfgOf<BF16, D, MASK, ROLE>;
   BwdParams p;
   p.q1 = static_cast<const char *>(a.q1);
   p.k1 = static_cast<const char *>(a.k1);
@@ -514,12 +574,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   const void *fn = reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN>);
-  if (C::kLdsBytes > 65536) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(C::kLdsBytes));
+  void *args[] = {&p};
+  const size_t dyn = size_t(2 * C::kStage + C::kXChunks) * 16 + 2 * C::kNCst * C::kBT * 4;
+  if (dyn > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
     if (e != hipSuccess) return e;
   }
-  void *args[] = {&p};
-  return hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
+  return hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, dyn, stream);
 }
 
 template <int ROLE, bool BF16, int D, bool CAUSAL>
