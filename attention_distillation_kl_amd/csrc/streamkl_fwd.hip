@@ -2,14 +2,18 @@
 //
 // StreamKL summary page (gist.science 2606.20005), "Formulazione Online":
 // KL(P1 || P2) of one query row is rewritten in terms of five running row
-// scalars -- the running maxima m1, m2 of the two logit rows, the unnormalised
-// exponential sums l1, l2 and an accumulator acc of the P1-weighted logit
-// difference -- finalised as KL = acc / l1 + LSE2 - LSE1, LSE_t = m_t + log l_t.
-// The page does not print the per-tile update; the one used here (the only
-// one for which that finaliser equals KL) is, for a tile of keys J:
-//   m_t' = max(m_t, max_J s_t)            alpha_t = exp(m_t - m_t')
-//   l_t  = alpha_t l_t + sum_J exp(s_t - m_t')
-//   acc  = alpha_1 acc + sum_J exp(s_1 - m_1') (s_1 - s_2)
+// scalars -- two shifts m1, m2 for the two logit rows (the page's running
+// maxima), the exponential sums l1, l2 taken against them and an accumulator
+// acc of the P1-weighted logit difference -- finalised as
+// KL = acc / l1 + LSE2 - LSE1, LSE_t = m_t + log l_t.  The page does not print
+// the per-tile update.  The rule used here, for a tile of keys J, is
+//   l_t = alpha_t l_t + sum_J exp(s_t - m_t'),  alpha_t = exp(m_t - m_t')
+//   acc = alpha_1 acc + sum_J exp(s_1 - m_1') (s_1 - s_2)
+// which makes acc / l1 = sum_j P1 (s1 - s2) for ANY sequence of shifts; the
+// finaliser then equals KL exactly.  The shifts only keep the exponentials in
+// range: m_t' = max(m_t, max_J s_t) would do, but computing a maximum per tile
+// costs as much as a sum, so a shift is raised only where a tile's sums would
+// leave [0, 2^64] (see `pass` and `raise_and_fold` below).
 // Key tiles past a query block's causal frontier are never visited.
 //
 // Mapping to the hardware:
@@ -17,14 +21,16 @@
 //     each wave keeps its queries' Q1/Q2 fragments in registers for the
 //     whole key loop, and every K fragment it reads from LDS feeds the
 //     products of both of its 32-query blocks;
-//   * K1/K2 tiles (64 keys for bf16, 32 for fp32) are staged in LDS, double
-//     buffered through registers, with an XOR chunk swizzle;
+//   * K1/K2 tiles (64 keys for bf16, 32 for fp32) are staged in LDS by direct
+//     global->LDS copies, double buffered, stored chunk-major;
 //   * scores are computed transposed (S^T = K Q^T, 32x32 MFMA blocks) so each
 //     lane owns ONE query and 16 keys of every 32-key block: the maxima and
 //     sums are in-lane, each lane-half keeps its own five scalars and the two
 //     halves are merged once, after the loop (the merge is the same rescale);
 //   * exponentials are exp2 with scale*log2(e) folded into one FMA; the
-//     maxima are tracked on raw dot products and scale is applied at the end.
+//     shifts are kept on raw dot products and scale is applied at the end;
+//   * a wave raises its priority while it issues its matrix products, so the
+//     other wave on the SIMD fills the vector unit meanwhile.
 #include "streamkl_device.h"
 #include "streamkl_launch.h"
 
@@ -67,7 +73,7 @@ void fwd_kernel(FwdParams p) {
   extern __shared__ u32x4 lds[];  // [stage][tensor][kTileChunks]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
 
   // Heads are contiguous in logical order (one head per XCD at a time);
@@ -123,68 +129,60 @@ void fwd_kernel(FwdParams p) {
   const char *kb2 = p.k2 + koff;
 
   // Stage key tile kt into LDS buffer `stage` with direct global->LDS copies.
-  // Lane L of wave w fills chunk position i*256 + 64w + L of the tile; the
-  // global side picks the (row, logical chunk) that belongs there under the
-  // XOR swizzle (its own inverse).  Rows past N_K repeat the last key; the
-  // compute masks them.
+  // The tile is stored chunk-major: 16-byte chunk c of tile row r sits at
+  // position c*kBK + r.  A lane's fragment chunks are then one base address
+  // plus compile-time offsets, and the 32 lanes of a half read 32 consecutive
+  // chunks (no bank conflicts).  Lane L of wave w fills position
+  // i*256 + 64w + L, i.e. reads chunk c of key row r from global memory.
+  // Rows past N_K repeat the last key; the compute masks them.
+  static_assert(C::kThreads % C::kBK == 0, "a thread copies one tile row");
+  const int crow = tid % C::kBK;                // the tile row this thread copies
+  const int cch = tid / C::kBK;                 // its first chunk; then every kThreads/kBK
   auto issue = [&](int kt, int stage) {
+    const int key = min(kt * C::kBK + crow, p.nk - 1);
+    const size_t o = size_t(key) * G::kRowBytes + cch * 16;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int pos = i * C::kThreads + tid;
-      const int row = pos / G::kChunks;
-      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
-      const int key = min(kt * C::kBK + row, p.nk - 1);
-      const size_t o = size_t(key) * G::kRowBytes + ch * 16;
+      const int oi = i * (C::kThreads / C::kBK) * 16;
       u32x4 *w1 = lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64;
       u32x4 *w2 = lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64;
-      dma16(kb1 + o, w1);
-      dma16(kb2 + o, w2);
+      dma16(kb1 + o + oi, w1);
+      dma16(kb2 + o + oi, w2);
     }
   };
 
   const float c = p.c;
-  // The five running scalars per query block and lane-half.
-  float m1[NQB], m2[NQB], l1[NQB], l2[NQB], acc[NQB];
+  // The five running scalars per query block and lane-half.  m1, m2 are the
+  // shifts the exponentials are taken against, in raw dot-product units.  They
+  // are not re-derived from every block's maximum: they only have to stay at
+  // or below the running maximum (so l_t >= 1) and close enough to it that no
+  // exponential overflows.  A block whose sums stay within kSumCap (every
+  // exponential then lies in [0, 2^64]) is folded as it is; otherwise -- the
+  // first admissible block, or logits more than 64 log2-units above the shift
+  // -- the lane raises its shifts to the block's maximum, rescales l and acc,
+  // and folds the block again.  Any shift yields the same finalised KL and LSE.
+  constexpr float kSumCap = 18446744073709551616.f;  // 2^64
+  float m1[NQB], m2[NQB], nm1c[NQB], nm2c[NQB], l1[NQB], l2[NQB], acc[NQB];
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     m1[j] = m2[j] = -INFINITY;
+    nm1c[j] = nm2c[j] = INFINITY;  // -m c
     l1[j] = l2[j] = acc[j] = 0.f;
   }
 
-  // Online update of query block j's scalars with one 32-key block of scores.
-  auto fold = [&](int j, const f32x16 &s1, const f32x16 &s2, int kb, auto masked_c) {
+  // Online update of query block j's scalars with one 32-key block of scores:
+  // fold against the current shifts; a lane whose sums leave the cap raises
+  // its shifts and folds the block again (every term is then <= 1).
+  auto pass = [&](int j, const f32x16 &s1, const f32x16 &s2, int kb, auto masked_c) -> bool {
     constexpr bool kMasked = decltype(masked_c)::value;
-    float ta1 = m1[j], tb1 = m1[j], ta2 = m2[j], tb2 = m2[j];
-    if constexpr (!kMasked) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        ta1 = vmax3(s1[r], s1[r + 1], ta1);
-        tb1 = vmax3(s1[r + 2], s1[r + 3], tb1);
-        ta2 = vmax3(s2[r], s2[r + 1], ta2);
-        tb2 = vmax3(s2[r + 2], s2[r + 3], tb2);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const bool oka = kb + c_row(r, h) <= my_last[j];
-        const bool okb = kb + c_row(r + 1, h) <= my_last[j];
-        ta1 = vmax(ta1, oka ? s1[r] : -INFINITY);
-        tb1 = vmax(tb1, okb ? s1[r + 1] : -INFINITY);
-        ta2 = vmax(ta2, oka ? s2[r] : -INFINITY);
-        tb2 = vmax(tb2, okb ? s2[r + 1] : -INFINITY);
-      }
-    }
-    const float tm1 = vmax(ta1, tb1), tm2 = vmax(ta2, tb2);
-    const float a1 = (m1[j] == -INFINITY) ? 0.f : fast_exp2((m1[j] - tm1) * c);
-    const float a2 = (m2[j] == -INFINITY) ? 0.f : fast_exp2((m2[j] - tm2) * c);
-    const float nm1c = -tm1 * c, nm2c = -tm2 * c;
-    float ts1a = 0.f, ts1b = 0.f, ts2a = 0.f, ts2b = 0.f, tda = 0.f, tdb = 0.f;
+    // -0 is the additive identity, so the sums start with their first term.
+    float ts1a = -0.f, ts1b = -0.f, ts2a = -0.f, ts2b = -0.f, tda = -0.f, tdb = -0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float p1a = fast_exp2(fmaf(s1[r], c, nm1c));
-      float p2a = fast_exp2(fmaf(s2[r], c, nm2c));
-      float p1b = fast_exp2(fmaf(s1[r + 1], c, nm1c));
-      float p2b = fast_exp2(fmaf(s2[r + 1], c, nm2c));
+      float p1a = fast_exp2(fmaf(s1[r], c, nm1c[j]));
+      float p2a = fast_exp2(fmaf(s2[r], c, nm2c[j]));
+      float p1b = fast_exp2(fmaf(s1[r + 1], c, nm1c[j]));
+      float p2b = fast_exp2(fmaf(s2[r + 1], c, nm2c[j]));
       if constexpr (kMasked) {
         const bool oka = kb + c_row(r, h) <= my_last[j];
         const bool okb = kb + c_row(r + 1, h) <= my_last[j];
@@ -200,11 +198,48 @@ void fwd_kernel(FwdParams p) {
       tda = fmaf(p1a, s1[r] - s2[r], tda);
       tdb = fmaf(p1b, s1[r + 1] - s2[r + 1], tdb);
     }
-    l1[j] = fmaf(l1[j], a1, ts1a + ts1b);
-    l2[j] = fmaf(l2[j], a2, ts2a + ts2b);
-    acc[j] = fmaf(acc[j], a1, tda + tdb);
-    m1[j] = tm1;
-    m2[j] = tm2;
+    const float ts1 = ts1a + ts1b, ts2 = ts2a + ts2b, td = tda + tdb;
+    const bool raise = ts1 > kSumCap || ts2 > kSumCap;
+    // Selects rather than a branch: the terms are consumed as they are made.
+    l1[j] += raise ? 0.f : ts1;
+    l2[j] += raise ? 0.f : ts2;
+    acc[j] += raise ? 0.f : td;
+    return raise;
+  };
+  // Scores of query block j alone against the 32 keys at tile row sb*32 of
+  // buffers (kb1s, kb2s): used where a block has to be folded again.
+  auto rescore = [&](int j, int sb, const u32x4 *t1, const u32x4 *t2, f32x16 &s1, f32x16 &s2) {
+    s1 = f32x16{};
+    s2 = f32x16{};
+    const int row = sb * 32 + col;
+#pragma unroll
+    for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+      const int pos = frag_chunk<BF16, D>(h, cc) * C::kBK + row;
+      mfma_chunk<BF16>(t1[pos], qf1[j][cc], s1);
+      mfma_chunk<BF16>(t2[pos], qf2[j][cc], s2);
+    }
+  };
+  // A raise (rare: the first admissible block of a row, or an overflow)
+  // happens after every query block's first pass, when no score register is
+  // live any more: the scores are recomputed from the tile, still in LDS.
+  auto raise_and_fold = [&](int j, const f32x16 &r1, const f32x16 &r2, int kb) {
+    float u1 = m1[j], u2 = m2[j];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok = kb + c_row(r, h) <= my_last[j];
+      u1 = vmax(u1, ok ? r1[r] : -INFINITY);
+      u2 = vmax(u2, ok ? r2[r] : -INFINITY);
+    }
+    const float a1 = (m1[j] == -INFINITY) ? 0.f : fast_exp2((m1[j] - u1) * c);
+    const float a2 = (m2[j] == -INFINITY) ? 0.f : fast_exp2((m2[j] - u2) * c);
+    l1[j] *= a1;
+    acc[j] *= a1;
+    l2[j] *= a2;
+    m1[j] = u1;
+    m2[j] = u2;
+    nm1c[j] = -u1 * c;
+    nm2c[j] = -u2 * c;
+    pass(j, r1, r2, kb, std::true_type{});
   };
 
   if (ntiles > 0) issue(0, 0);
@@ -231,9 +266,10 @@ void fwd_kernel(FwdParams p) {
         s2[j] = f32x16{};
       }
       const int row = sb * 32 + col;
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-        const int pos = row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc));
+        const int pos = frag_chunk<BF16, D>(h, cc) * C::kBK + row;
         const u32x4 a1 = b1[pos], a2 = b2[pos];
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
@@ -251,20 +287,37 @@ void fwd_kernel(FwdParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
 
       // Fold each query block: plain when the whole block is admissible.
-      bool plain = true;
+      bool plain = true, rz[NQB];
 #pragma unroll
-      for (int j = 0; j < NQB; ++j) plain = plain && kb + 31 <= blk_lo[j];
+      for (int j = 0; j < NQB; ++j) {
+        plain = plain && kb + 31 <= blk_lo[j];
+        rz[j] = false;
+      }
       if (plain) {
 #pragma unroll
-        for (int j = 0; j < NQB; ++j) fold(j, s1[j], s2[j], kb, std::false_type{});
+        for (int j = 0; j < NQB; ++j) rz[j] = pass(j, s1[j], s2[j], kb, std::false_type{});
       } else {
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
           if (kb > blk_hi[j]) continue;
-          if (kb + 31 > blk_lo[j]) fold(j, s1[j], s2[j], kb, std::true_type{});
-          else fold(j, s1[j], s2[j], kb, std::false_type{});
+          if (kb + 31 > blk_lo[j]) rz[j] = pass(j, s1[j], s2[j], kb, std::true_type{});
+          else rz[j] = pass(j, s1[j], s2[j], kb, std::false_type{});
+        }
+      }
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) any = any || rz[j];
+      // Wave-uniform branches: the products of a recompute need every lane.
+      if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) {
+          if (__builtin_amdgcn_ballot_w64(rz[j]) == 0) continue;
+          f32x16 r1, r2;
+          rescore(j, sb, b1, b2, r1, r2);
+          if (rz[j]) raise_and_fold(j, r1, r2, kb);
         }
       }
     }
