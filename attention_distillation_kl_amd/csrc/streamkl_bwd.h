@@ -103,11 +103,12 @@ struct BwdParams {
 //    P_t = exp2(s_t c - L_t); g (1 without an upstream gradient);
 //    dp = delta / scale with delta = KL + LSE1 - LSE2.  Rows past N_Q get
 //    L_t = inf, which makes every P they enter zero.
-//  ROLE_DK (streamed queries, in LDS per tile): cs_t = -LSE_t / scale, used as
-//    the initial accumulator of the score products so they yield
-//    s_t' = s_t - LSE_t / scale and P_t = exp2(s_t' c); then
-//    s1 - s2 - delta/scale = s1' - s2' - KL/scale, so the only per-element
-//    constant left is gk = g KL / scale (and g itself when g varies).
+//  ROLE_DK (streamed queries, in LDS per tile): the initial accumulators of
+//    the score products are -LSE1/scale and (KL - LSE2)/scale, so they yield
+//    s1' = s1 - LSE1/scale and s2'' = s2 + (KL - LSE2)/scale; then
+//    P1 = exp2(s1' c), P2 = exp2(s2'' c - KL c/scale) and
+//    s1 - s2 - delta/scale = s1' - s2''.  The per-element constants left are
+//    kc = -KL c/scale (and g itself when g varies).
 struct RowCst {
   float l1, l2, g, dp;
 };
@@ -270,12 +271,12 @@ void bwd_kernel(BwdParams p) {
   };
   auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
-      // Rows past N_Q: -1e30 (not -inf) keeps s1' - s2' finite (0) and P = 0.
+      // Rows past N_Q: -1e30 (not -inf) keeps s1' - s2'' finite (0) and P = 0.
       float *cst = cstage[stage];
       cst[tid] = n_ok ? -n_lse1 * p.inv_scale : -1e30f;
-      cst[C::kBT + tid] = n_ok ? -n_lse2 * p.inv_scale : -1e30f;
+      cst[C::kBT + tid] = n_ok ? (n_kl - n_lse2) * p.inv_scale : -1e30f;
       cst[2 * C::kBT + tid] = n_ok ? n_g : 0.f;
-      cst[3 * C::kBT + tid] = n_ok ? n_g * n_kl * p.inv_scale : 0.f;
+      cst[3 * C::kBT + tid] = n_ok ? -n_kl * p.inv_scale * p.c : 0.f;
     }
   };
 
@@ -319,10 +320,22 @@ void bwd_kernel(BwdParams p) {
     const u32x4 *ybase = stage ? ystage1 : ystage0;
     const float *cst = cstage[stage];
 
-    // 1. recompute the two score blocks of block sb
-    auto scores = [&](int sb, f32x16 &s1, f32x16 &s2) {
+    // Whether block sb holds an inadmissible (streamed, stationary) pair for
+    // any lane of this wave: a causal frontier or the end of the streamed rows
+    // passes through it (wave-uniform).
+    auto straddles = [&](int sb) {
+      const int tb = tile * C::kBT + sb * 32;
+      if (ROLE == ROLE_DQ) return tb + 31 > (CAUSAL ? min(w0 + off, p.nk - 1) : p.nk - 1);
+      return tb + 31 > p.nq - 1 || (CAUSAL && tb < max(w0 + 31 - off, 0));
+    };
+
+    // 1. recompute the two score blocks of block sb.  Inadmissible pairs start
+    //    from -1e30 instead of their row constant: their P is then exactly 0
+    //    and s1 - s2 is 0 (both products are absorbed), so e1 = e2 = 0 with no
+    //    mask in the per-element work.  Only blocks that straddle pay for it.
+    auto scores = [&](int sb, f32x16 &s1, f32x16 &s2, bool masked) {
       if (ROLE == ROLE_DK) {
-        // initial accumulators -LSE_t/scale of the block's rows, in C layout
+        // initial accumulators of the block's rows, in C layout
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int r0 = sb * 32 + g4 * 8 + 4 * h;
@@ -337,6 +350,17 @@ void bwd_kernel(BwdParams p) {
       } else {
         s1 = f32x16{};
         s2 = f32x16{};
+      }
+      if (masked) {
+        // Element r sits at streamed row rel + c_row(r, 0).
+        const int rel = tile * C::kBT + sb * 32 + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = rel + c_row(r, 0);
+          const bool ok = ROLE == ROLE_DQ ? t <= lim : (t >= lim && t < p.nq);
+          s1[r] = ok ? s1[r] : -1e30f;
+          s2[r] = ok ? s2[r] : -1e30f;
+        }
       }
       const int arow = sb * 32 + col;
       const int xrow = wrow * 32 + col;  // the lane's stationary row in the LDS tile
@@ -354,48 +378,34 @@ void bwd_kernel(BwdParams p) {
       }
     };
 
-    // 2. regenerate P and form e1, e2 (fp32); the admissibility mask is
-    //    applied only on blocks that straddle a frontier or the end.
-    auto form = [&](int sb, const f32x16 &s1, const f32x16 &s2, EBlock &E, auto masked_c) {
-      constexpr bool kMasked = decltype(masked_c)::value;
-      // Element r sits at streamed row tb + c_row(r, 0) + 4h: compare the
-      // compile-time part against per-lane bounds taken once per block.
-      const int rel = tile * C::kBT + sb * 32 + 4 * h;
-      const int lo = ROLE == ROLE_DQ ? INT_MIN : lim - rel;
-      const int hi = ROLE == ROLE_DQ ? lim - rel : p.nq - 1 - rel;
+    // 2. regenerate P and form e1, e2 (fp32).
+    auto form = [&](int sb, const f32x16 &s1, const f32x16 &s2, EBlock &E) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 Gv, GKv;
+        f32x4 Gv, KCv;
         if (ROLE == ROLE_DK) {
           const int r0 = sb * 32 + g4 * 8 + 4 * h;
           if (GSIGN) Gv = *reinterpret_cast<const f32x4 *>(cst + 2 * C::kBT + r0);
-          GKv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
+          KCv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = g4 * 4 + q;
-          float p1, p2;
-          if (ROLE == ROLE_DK) {  // s_t already carry -LSE_t/scale
-            p1 = fast_exp2(s1[r] * c);
-            p2 = kG2 ? fast_exp2(s2[r] * c) : 0.f;
+          if (ROLE == ROLE_DK) {  // s1' and s2'' carry their row constants
+            const float p1 = fast_exp2(s1[r] * c);
+            const float p2 = kG2 ? fast_exp2(fmaf(s2[r], c, KCv[q])) : 0.f;
+            if (GSIGN) {
+              const float gp1 = p1 * Gv[q];
+              E.e2[r] = fmaf(p2, Gv[q], -gp1);
+              E.e1[r] = gp1 * (s1[r] - s2[r]);
+            } else {
+              E.e2[r] = p2 - p1;
+              E.e1[r] = p1 * (s1[r] - s2[r]);
+            }
           } else {
-            p1 = fast_exp2(fmaf(s1[r], c, -rc.l1));
-            p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -rc.l2)) : 0.f;
-          }
-          if constexpr (kMasked) {
-            const int cr = c_row(r, 0);  // a constant after unrolling
-            const bool ok = ROLE == ROLE_DQ ? cr <= hi : (cr >= lo && cr <= hi);
-            p1 = ok ? p1 : 0.f;
-            p2 = ok ? p2 : 0.f;
-          }
-          if (ROLE == ROLE_DK && GSIGN) {
-            E.e2[r] = (p2 - p1) * Gv[q];
-            E.e1[r] = p1 * fmaf(s1[r] - s2[r], Gv[q], -GKv[q]);
-          } else if (ROLE == ROLE_DK) {
-            E.e2[r] = p2 - p1;
-            E.e1[r] = p1 * ((s1[r] - s2[r]) - GKv[q]);
-          } else {
-            // ROLE_DQ: dp of the lane's own row; g is applied at write-out.
+            // ROLE_DQ: constants of the lane's own row; g is applied at write-out.
+            const float p1 = fast_exp2(fmaf(s1[r], c, -rc.l1));
+            const float p2 = kG2 ? fast_exp2(fmaf(s2[r], c, -rc.l2)) : 0.f;
             E.e2[r] = p2 - p1;
             E.e1[r] = p1 * ((s1[r] - s2[r]) - rc.dp);
           }
@@ -459,15 +469,12 @@ void bwd_kernel(BwdParams p) {
       }
     };
 
-    // One straight-line path for every tile: the mask costs a compare and
-    // two selects per element, cheaper than a second copy of the loop body
-    // competing for the same 256 registers.  Blocks wholly outside the
-    // admissible region contribute exact zeros.
+    // Blocks wholly outside the admissible region contribute exact zeros.
     if constexpr (kPair) {
       f32x16 s1, s2;
       EBlock E;
-      scores(half, s1, s2);
-      form(half, s1, s2, E, std::true_type{});
+      scores(half, s1, s2, straddles(half));
+      form(half, s1, s2, E);
       // Keep the operand of the gradient this wave accumulates; hand the
       // other to the partner, which scored the other block.
       u32x4 mine[2], theirs[2], b0[2], b1[2];
@@ -499,8 +506,8 @@ void bwd_kernel(BwdParams p) {
       for (int sb = 0; sb < C::kSub; ++sb) {
         f32x16 s1, s2;
         EBlock E;
-        scores(sb, s1, s2);
-        form(sb, s1, s2, E, std::true_type{});
+        scores(sb, s1, s2, straddles(sb));
+        form(sb, s1, s2, E);
         grad(sb, E);
         __builtin_amdgcn_sched_barrier(0);
       }
