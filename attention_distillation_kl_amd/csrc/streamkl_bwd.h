@@ -364,6 +364,10 @@ void bwd_kernel(BwdParams p) {
       }
       const int arow = sb * 32 + col;
       const int xrow = wrow * 32 + col;  // the lane's stationary row in the LDS tile
+      // Without pairing, the MFMA bursts run at raised priority so that the
+      // other wave on the SIMD keeps the vector unit busy meanwhile (paired
+      // waves gain nothing from it).
+      if (!kPair) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
         const int fc = frag_chunk<BF16, D>(h, cc);
@@ -376,6 +380,7 @@ void bwd_kernel(BwdParams p) {
         }
         mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
       }
+      if (!kPair) __builtin_amdgcn_s_setprio(0);
     };
 
     // 2. regenerate P and form e1, e2 (fp32).
@@ -428,6 +433,7 @@ void bwd_kernel(BwdParams p) {
     //    4h + s/4, columns mb*32 + 16(grp&1) + 4(s&3) .. +3.
     auto grad_bf16 = [&](int sb, const char *yb, const u32x4 (&pk)[2], f32x16 (&acc)[kMB]) {
       const int s16 = lane & 15, grp = lane >> 4;
+      if (!kPair) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -445,6 +451,7 @@ void bwd_kernel(BwdParams p) {
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                              __builtin_bit_cast(bf16x8, pk[ks]), acc[mb], 0, 0, 0);
         }
+      if (!kPair) __builtin_amdgcn_s_setprio(0);
     };
     auto grad = [&](int sb, const EBlock &E) {
       if constexpr (BF16) {
