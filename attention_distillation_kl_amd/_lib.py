@@ -13,7 +13,8 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 GRAD_Q1K1, GRAD_Q2K2, GRAD_ALL = 1, 2, 3
 
-EXPORTS = ("streamkl_fwd", "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_splits", "streamkl_fwd_workspace_size", "streamkl_fwd_splitk",
+           "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk",
            "streamkl_bwd_workspace_size", "streamkl_status_str", "streamkl_abi_version")
 
 
@@ -39,6 +40,13 @@ def load(path: str = LIB_PATH):
     lib.streamkl_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
                                  _fp, _fp, _fp, _vp]
     lib.streamkl_fwd.restype = _i
+    lib.streamkl_fwd_splits.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    lib.streamkl_fwd_splits.restype = _i
+    lib.streamkl_fwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    lib.streamkl_fwd_workspace_size.restype = _sz
+    lib.streamkl_fwd_splitk.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
+                                        _fp, _fp, _fp, _vp, _sz, _vp]
+    lib.streamkl_fwd_splitk.restype = _i
     lib.streamkl_bwd.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
                                  _f, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.streamkl_bwd.restype = _i
@@ -70,6 +78,21 @@ def fwd(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, kl, lse1, lse2, s
     """Raw call with integer addresses; returns the status code."""
     return load().streamkl_fwd(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype,
                                kl, lse1, lse2, stream)
+
+
+def fwd_splits(B, H, NQ, NK, d, causal, dtype):
+    """The library's choice of key partitions for the split-K forward (1 = none)."""
+    return load().streamkl_fwd_splits(B, H, NQ, NK, d, causal, dtype)
+
+
+def fwd_workspace_size(B, H, NQ, NK, d, causal, dtype, splits):
+    return load().streamkl_fwd_workspace_size(B, H, NQ, NK, d, causal, dtype, splits)
+
+
+def fwd_splitk(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits, kl, lse1, lse2,
+               workspace, workspace_bytes, stream):
+    return load().streamkl_fwd_splitk(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits,
+                                      kl, lse1, lse2, workspace, workspace_bytes, stream)
 
 
 def bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,

@@ -63,6 +63,43 @@ streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2, con
                                                                                   : STREAMKL_ERR_HIP;
 }
 
+int streamkl_fwd_splits(int B, int H, int N_Q, int N_K, int d, int causal, int dtype) {
+  (void)causal;
+  if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return 1;
+  if (dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) return 1;
+  const long long bh = (long long)B * H;
+  if (bh > INT32_MAX) return 1;
+  return streamkl::fwd_default_splits(int(bh), N_Q, N_K, d, dtype == STREAMKL_BF16);
+}
+
+size_t streamkl_fwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype, int splits) {
+  (void)N_K, (void)d, (void)causal, (void)dtype;
+  if (splits <= 1 || B <= 0 || H <= 0 || N_Q <= 0) return 0;
+  return size_t(5) * size_t(splits) * size_t(B) * size_t(H) * size_t(N_Q) * sizeof(float);
+}
+
+streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1, const void *q2, const void *k2, int B,
+                                    int H, int N_Q, int N_K, int d, float scale, int causal, int dtype,
+                                    int splits, float *kl, float *lse1, float *lse2, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  streamkl_status s = check_common(q1, k1, q2, k2, B, H, N_Q, N_K, d, scale, causal, dtype);
+  if (s != STREAMKL_OK) return s;
+  if (splits < 1 || splits > STREAMKL_MAX_SPLITS) return STREAMKL_ERR_INVALID_ARGUMENT;
+  const long long rows = (long long)B * H * N_Q;
+  if (!row_vec_ok(kl, rows) || !row_vec_ok(lse1, rows) || !row_vec_ok(lse2, rows))
+    return STREAMKL_ERR_INVALID_ARGUMENT;
+  const size_t need = streamkl_fwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, splits);
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
+    return STREAMKL_ERR_WORKSPACE;
+  if (rows == 0) return STREAMKL_OK;
+  streamkl::FwdArgs a{q1, k1, q2, k2, kl, lse1, lse2, B * H, N_Q, N_K, d, scale, causal != 0,
+                      dtype == STREAMKL_BF16};
+  a.splits = splits;
+  a.part = static_cast<float *>(workspace);
+  return streamkl::launch_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
+                                                                                  : STREAMKL_ERR_HIP;
+}
+
 size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype,
                                    int grad_mask) {
   (void)B, (void)H, (void)N_Q, (void)N_K, (void)d, (void)causal, (void)dtype, (void)grad_mask;

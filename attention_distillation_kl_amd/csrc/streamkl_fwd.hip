@@ -34,6 +34,7 @@
 #include "streamkl_device.h"
 #include "streamkl_launch.h"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -62,9 +63,18 @@ struct FwdParams {
   float *kl, *lse1, *lse2;
   int nq, nk, nqb;
   float scale, c;  // c = scale * log2(e)
+  // Split-K: the key tiles are dealt to nsplit partitions of tps tiles each;
+  // partition states go to part = [5][nsplit][bh * nq] (m1, m2, l1, l2, acc).
+  int nsplit, tps;
+  size_t rows;  // B * H * N_Q
+  float *part;
 };
 
-template <bool BF16, int D, bool CAUSAL>
+// Row-state layout of the split-K workspace: scalar k of partition s for
+// row r (r = bh * N_Q + i) of `rows` rows lives at part[(k * nsplit + s) * rows + r].
+enum { ST_M1 = 0, ST_M2, ST_L1, ST_L2, ST_ACC, ST_N };
+
+template <bool BF16, int D, bool CAUSAL, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
   using C = FwdCfg<BF16, D>;
@@ -78,9 +88,14 @@ void fwd_kernel(FwdParams p) {
 
   // Heads are contiguous in logical order (one head per XCD at a time);
   // for causal problems the longest query blocks of a head go first.
+  // With split-K, the query blocks of one (head, partition) are consecutive,
+  // so they share the partition's K tiles in one L2.
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = bid / p.nqb;
-  const int qbr = bid - bh * p.nqb;
+  const int per_bh = p.nqb * (SPLIT ? p.nsplit : 1);
+  const int bh = bid / per_bh;
+  const int rem = bid - bh * per_bh;
+  const int split = SPLIT ? rem / p.nqb : 0;
+  const int qbr = rem - split * p.nqb;
   const int qb = CAUSAL ? p.nqb - 1 - qbr : qbr;
   const int q0 = qb * C::kBQ;
   const int wq0 = q0 + wave * C::kWQ;
@@ -112,7 +127,13 @@ void fwd_kernel(FwdParams p) {
   const int off = p.nk - p.nq;
   int kend = p.nk;
   if (CAUSAL) kend = min(p.nk, min(q0 + C::kBQ, p.nq) + off);
-  const int ntiles = (kend + C::kBK - 1) / C::kBK;
+  // Tiles [tile0, tile1) of this workgroup: the partition's share of them.
+  int tile0 = 0, tile1 = (kend + C::kBK - 1) / C::kBK;
+  if (SPLIT) {
+    tile0 = split * p.tps;
+    tile1 = min(tile1, tile0 + p.tps);
+  }
+  const int ntiles = max(tile1 - tile0, 0);
   // Per 32-query block j of the wave: the lane's last key, and the smallest
   // and largest last key over the block (wave-uniform).
   int my_last[NQB], blk_lo[NQB], blk_hi[NQB];
@@ -242,13 +263,13 @@ void fwd_kernel(FwdParams p) {
     pass(j, r1, r2, kb, std::true_type{});
   };
 
-  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0) issue(tile0, 0);
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
+  for (int kt = tile0; kt < tile1; ++kt) {
+    const int stage = (kt - tile0) & 1;
     // Buffer stage^1 was last read in iteration kt-1, which ended in a barrier.
-    if (kt + 1 < ntiles) issue(kt + 1, stage ^ 1);
+    if (kt + 1 < tile1) issue(kt + 1, stage ^ 1);
     const u32x4 *b1 = lds + (stage * 2 + 0) * C::kTileChunks;
     const u32x4 *b2 = lds + (stage * 2 + 1) * C::kTileChunks;
 
@@ -339,6 +360,20 @@ void fwd_kernel(FwdParams p) {
     const float L2 = l2[j] * fa2 + ol2 * fb2;
     const float A = acc[j] * fa1 + oacc * fb1;
     const int qrow = wq0 + 32 * j + col;
+    if (SPLIT) {
+      // The partition's state, merged with the others by merge_kernel.
+      if (h == 0 && qrow < p.nq) {
+        const size_t r = size_t(bh) * p.nq + qrow;
+        float *out = p.part + size_t(split) * p.rows + r;
+        const size_t stride = size_t(p.nsplit) * p.rows;
+        out[ST_M1 * stride] = M1;
+        out[ST_M2 * stride] = M2;
+        out[ST_L1 * stride] = L1;
+        out[ST_L2 * stride] = L2;
+        out[ST_ACC * stride] = A;
+      }
+      continue;
+    }
     if (h == 0 && qrow < p.nq) {
       const float lse1 = M1 * p.scale + logf(L1);
       const float lse2 = M2 * p.scale + logf(L2);
@@ -348,6 +383,38 @@ void fwd_kernel(FwdParams p) {
       p.lse2[o] = lse2;
     }
   }
+}
+
+// Split-K merge: one thread per row combines the partitions' states with the
+// rescale of the online update (empty partitions, m = -inf, weigh 0) and
+// finalises the row as the unsplit kernel does.  With one partition it
+// reproduces the unsplit results bit for bit.
+__global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part, int nsplit, size_t rows,
+                                                    float scale, float c, float *kl, float *lse1, float *lse2) {
+  const size_t r = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const size_t stride = size_t(nsplit) * rows;
+  const float *st = part + r;
+  float M1 = -INFINITY, M2 = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) {
+    M1 = vmax(M1, st[ST_M1 * stride + size_t(s) * rows]);
+    M2 = vmax(M2, st[ST_M2 * stride + size_t(s) * rows]);
+  }
+  float L1 = 0.f, L2 = 0.f, A = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t o = size_t(s) * rows;
+    const float m1 = st[ST_M1 * stride + o], m2 = st[ST_M2 * stride + o];
+    const float f1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - M1) * c);
+    const float f2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - M2) * c);
+    L1 = fmaf(st[ST_L1 * stride + o], f1, L1);
+    L2 = fmaf(st[ST_L2 * stride + o], f2, L2);
+    A = fmaf(st[ST_ACC * stride + o], f1, A);
+  }
+  const float l1 = M1 * scale + logf(L1);
+  const float l2 = M2 * scale + logf(L2);
+  kl[r] = scale * (A / L1) + l2 - l1;
+  lse1[r] = l1;
+  lse2[r] = l2;
 }
 
 template <bool BF16, int D, bool CAUSAL>
@@ -366,15 +433,44 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   p.nqb = (a.nq + C::kBQ - 1) / C::kBQ;
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
-  const long long blocks = (long long)p.nqb * a.bh;
+  p.rows = size_t(a.bh) * a.nq;
+  const bool split = a.splits > 1;
+  const int total_tiles = (a.nk + C::kBK - 1) / C::kBK;
+  p.nsplit = split ? a.splits : 1;
+  p.tps = (total_tiles + p.nsplit - 1) / p.nsplit;
+  p.part = a.part;
+  const long long blocks = (long long)p.nqb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   void *args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL>),
-                         dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
+  const void *fn = split ? reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, true>)
+                         : reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, false>);
+  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
+  if (e != hipSuccess || !split) return e;
+  const size_t mblocks = (p.rows + 255) / 256;
+  if (mblocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
+  merge_kernel<<<dim3(unsigned(mblocks)), dim3(256), 0, stream>>>(a.part, p.nsplit, p.rows, p.scale, p.c, a.kl,
+                                                                  a.lse1, a.lse2);
+  return hipGetLastError();
 }
 
 }  // namespace
+
+int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16) {
+  // Partitions of the key dimension so that the grid holds about four
+  // workgroups per CU (two resident, two queued), each partition keeping at
+  // least four key tiles.  Grids that are already that large are not split.
+  const bool nqb2 = bf16 || d == 64;
+  const int kbq = nqb2 ? 256 : 128, kbk = bf16 ? 64 : 32;
+  const long long nwg = (long long)bh * ((nq + kbq - 1) / kbq);
+  if (nwg <= 0) return 1;
+  constexpr long long kTarget = 1024;
+  if (nwg >= kTarget) return 1;
+  const long long tiles = (nk + kbk - 1) / kbk;
+  long long s = (kTarget + nwg - 1) / nwg;
+  s = std::min(s, std::max(1LL, tiles / 4));
+  return int(std::min(s, 256LL));
+}
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
   if (a.bf16) {

@@ -13,6 +13,8 @@ struct FwdArgs {
   int bh, nq, nk, d;
   float scale;
   bool causal, bf16;
+  int splits = 1;           // key partitions (split-K) when > 1
+  float *part = nullptr;    // their row states: 5 * splits * bh * nq floats
 };
 
 struct BwdArgs {
@@ -26,6 +28,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+// The library's choice of key partitions for a forward problem (1 = none).
+int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16);
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
 

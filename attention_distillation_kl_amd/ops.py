@@ -46,18 +46,35 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False):
-    """Per-row (KL(P1||P2), LSE1, LSE2), each [B, H, N_Q] float32."""
+def streamkl_fwd(q1, k1, q2, k2, scale=None, causal=False, splits=None):
+    """Per-row (KL(P1||P2), LSE1, LSE2), each [B, H, N_Q] float32.
+
+    ``splits``: key partitions of the split-K forward; None takes the
+    library's choice (streamkl_fwd_splits), 1 runs the unsplit kernel.  The
+    partitions' row states live in a workspace allocated here with torch."""
     B, H, NQ, NK, d = _check_inputs(q1, k1, q2, k2)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q1.device
+    dt = _dtype_code(q1)
+    causal = int(bool(causal))
     kl = torch.empty(B, H, NQ, device=dev, dtype=torch.float32)
     lse1 = torch.empty_like(kl)
     lse2 = torch.empty_like(kl)
-    st = _lib.fwd(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), B, H, NQ, NK, d, scale, int(bool(causal)),
-                  _dtype_code(q1), _ptr(kl), _ptr(lse1), _ptr(lse2), _stream(dev))
+    if splits is None:
+        splits = _lib.fwd_splits(B, H, NQ, NK, d, causal, dt)
+    splits = int(splits)
+    if splits == 1:
+        st = _lib.fwd(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), B, H, NQ, NK, d, scale, causal,
+                      dt, _ptr(kl), _ptr(lse1), _ptr(lse2), _stream(dev))
+        where = "streamkl_fwd"
+    else:
+        ws_bytes = _lib.fwd_workspace_size(B, H, NQ, NK, d, causal, dt, splits)
+        ws = torch.empty(max(1, (ws_bytes + 3) // 4), device=dev, dtype=torch.float32)
+        st = _lib.fwd_splitk(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), B, H, NQ, NK, d, scale, causal,
+                             dt, splits, _ptr(kl), _ptr(lse1), _ptr(lse2), _ptr(ws), ws_bytes, _stream(dev))
+        where = "streamkl_fwd_splitk"
     if st != _lib.OK:
-        raise _lib.StreamKLError(st, "streamkl_fwd")
+        raise _lib.StreamKLError(st, where)
     return kl, lse1, lse2
 
 

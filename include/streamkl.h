@@ -84,6 +84,55 @@ streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2,
                              int d, float scale, int causal, int dtype,
                              float *kl, float *lse1, float *lse2, void *stream);
 
+/* Largest key-partition count streamkl_fwd_splitk accepts. */
+#define STREAMKL_MAX_SPLITS 1024
+
+/*
+ * streamkl_fwd_splits -- the library's choice of key partitions for
+ * streamkl_fwd_splitk on this problem: enough that short query blocks (few
+ * workgroups per head, e.g. N_Q = 1 decoding or 2K queries over 64K keys)
+ * still fill every compute unit, at least four key tiles per partition, and
+ * 1 (no split) when the unsplit grid already fills the GPU.  Invalid sizes
+ * give 1.
+ */
+int streamkl_fwd_splits(int B, int H, int N_Q, int N_K, int d, int causal, int dtype);
+
+/*
+ * streamkl_fwd_workspace_size -- bytes of device workspace streamkl_fwd_splitk
+ * needs for `splits` partitions: 5 * splits * B * H * N_Q floats (the five
+ * running row scalars of every partition), 0 when splits <= 1.
+ */
+size_t streamkl_fwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
+                                   int causal, int dtype, int splits);
+
+/*
+ * streamkl_fwd_splitk -- streamkl_fwd with the key dimension partitioned over
+ * `splits` workgroups per query block ("Ottimizzazioni del Kernel GPU",
+ * Split-K bullet: for small query counts the keys are partitioned across
+ * thread blocks to fill the machine).  Partition s folds key tiles
+ * [s*T, (s+1)*T), T = ceil(ceil(N_K / tile) / splits), into the five running
+ * scalars of each row and stores them in `workspace`; a second kernel merges
+ * the partitions with the same rescale as the online update
+ * (m = max m_s, l = sum l_s exp(m_s - m), acc = sum acc_s exp(m1_s - m1)) and
+ * finalises kl, lse1, lse2.  Results equal streamkl_fwd's up to the order of
+ * floating-point summation; with splits == 1 they are identical.
+ *   splits: 1 .. STREAMKL_MAX_SPLITS (see streamkl_fwd_splits).
+ *   workspace / workspace_bytes: device memory of at least
+ *        streamkl_fwd_workspace_size(...) bytes, 16-byte aligned (may be NULL
+ *        when that is 0), owned by the caller, overwritten; its contents are
+ *        dead once the call's work has completed on `stream`.
+ * Errors as streamkl_fwd, plus STREAMKL_ERR_INVALID_ARGUMENT for a split
+ * count out of range and STREAMKL_ERR_WORKSPACE for a missing, misaligned
+ * or short workspace.
+ */
+streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1,
+                                    const void *q2, const void *k2, int B,
+                                    int H, int N_Q, int N_K, int d,
+                                    float scale, int causal, int dtype,
+                                    int splits, float *kl, float *lse1,
+                                    float *lse2, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /*
  * streamkl_bwd_workspace_size -- bytes of device workspace streamkl_bwd needs
  * for these arguments.  The two-kernel recompute backward needs none (0).

@@ -108,6 +108,49 @@ def test_empty_problems_are_noops(lib):
                dq1=None, dk1=None, dq2=None, dk2=None) == _lib.OK
 
 
+def fwd_splitk(**kw):
+    a = dict(q1=A, k1=A2, q2=A3, k2=A4, B=1, H=2, NQ=64, NK=4096, d=128, scale=0.125, causal=0,
+             dtype=_lib.BF16, splits=4, kl=O1, lse1=O2, lse2=O3, ws=0xC0000, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = _lib.fwd_workspace_size(a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["causal"], a["dtype"],
+                                           a["splits"])
+    return _lib.fwd_splitk(a["q1"], a["k1"], a["q2"], a["k2"], a["B"], a["H"], a["NQ"], a["NK"], a["d"],
+                           a["scale"], a["causal"], a["dtype"], a["splits"], a["kl"], a["lse1"], a["lse2"],
+                           a["ws"], a["wsb"], a["stream"])
+
+
+def test_splitk_workspace_size_is_five_states_per_row_and_partition(lib):
+    assert _lib.fwd_workspace_size(2, 3, 100, 5000, 128, 0, _lib.BF16, 7) == 5 * 7 * 2 * 3 * 100 * 4
+    assert _lib.fwd_workspace_size(2, 3, 100, 5000, 128, 0, _lib.BF16, 1) == 0
+    assert _lib.fwd_workspace_size(2, 3, 0, 5000, 128, 0, _lib.BF16, 7) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(splits=0), INV), (dict(splits=-2), INV), (dict(splits=1025), INV),
+    (dict(ws=None), _lib.ERR_WORKSPACE), (dict(wsb=16), _lib.ERR_WORKSPACE),
+    (dict(ws=0xC0004), _lib.ERR_WORKSPACE),
+    (dict(d=96), UNS), (dict(scale=0.0), INV), (dict(kl=None), INV), (dict(NQ=65, NK=64, causal=1), INV),
+])
+def test_fwd_splitk_rejects_bad_arguments(lib, kw, status):
+    assert fwd_splitk(**kw) == status
+
+
+def test_fwd_splitk_single_partition_needs_no_workspace(lib, no_gpu):
+    assert fwd_splitk(splits=1, ws=None, wsb=0) == _lib.ERR_HIP
+
+
+def test_default_split_choice(lib):
+    # short query block over long keys: split; a grid that fills the GPU: not
+    assert _lib.fwd_splits(1, 32, 2048, 65536, 128, 0, _lib.BF16) > 1
+    assert _lib.fwd_splits(1, 32, 32768, 32768, 128, 1, _lib.BF16) == 1
+    assert _lib.fwd_splits(1, 1, 1, 64, 128, 0, _lib.BF16) == 1      # one key tile: nothing to split
+    assert _lib.fwd_splits(0, 1, 1, 64, 128, 0, _lib.BF16) == 1      # invalid sizes
+    for nq, nk in ((1, 65536), (1, 1 << 20), (64, 4096)):
+        s = _lib.fwd_splits(1, 8, nq, nk, 128, 0, _lib.BF16)
+        assert 1 <= s <= 1024 and (nk + 63) // 64 >= 4 * s
+
+
 def test_workspace_query_is_zero_for_two_kernel_backward(lib):
     for mask in (1, 2, 3):
         assert _lib.bwd_workspace_size(2, 32, 8192, 8192, 128, 1, _lib.BF16, mask) == 0
