@@ -128,6 +128,32 @@ def test_fwd_peaked_and_large_inputs(dt):
     assert torch.isfinite(kl).all()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_logits_that_rise_or_fall_along_the_keys(dt, direction, causal):
+    """Keys along a common direction u with a linear ramp: the logits of
+    every row grow (direction 1) by about 1.5 per key, i.e. by more than 64
+    log2 units per 32-key block, so the running shift must be raised on
+    every block; or they fall (direction -1), so the first block's maximum
+    holds for the whole row.  The bound is relative to |LSE| as for the
+    other inputs far outside unit scale."""
+    g = torch.Generator(device=DEV).manual_seed(77)
+    NQ, NK, d = 96, 700, 64
+    u = torch.randn(d, device=DEV, generator=g)
+    u = u / u.norm()
+    ramp = torch.arange(NK, device=DEV, dtype=torch.float32)
+    if direction < 0:
+        ramp = ramp.flip(0)
+    def keys():
+        return (ramp[:, None] / 8.0) * u + 0.3 * torch.randn(NK, d, device=DEV, generator=g)
+    def queries():
+        return 12.0 * u + 0.3 * torch.randn(NQ, d, device=DEV, generator=g)
+    q1, k1, q2, k2 = (x[None, None].to(DT[dt]).contiguous() for x in (queries(), keys(), queries(), keys()))
+    kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, causal, tag=f"ramp {direction}", by_magnitude=True)
+    assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
+
+
 def test_fwd_is_deterministic():
     q1, k1, q2, k2 = make_inputs(1, 4, 1024, 1024, 128, torch.bfloat16, "student", 0.2, seed=9, device=DEV)
     a = ops.streamkl_fwd(q1, k1, q2, k2, 0.09, True)
