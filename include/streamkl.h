@@ -11,9 +11,10 @@
  *   KL[i] = KL(P1[i,:] || P2[i,:])
  *
  * computed in one pass over key tiles with five running row scalars
- * (two running maxima, two running exponential sums and one accumulator of
- * the P1-weighted logit difference), finalised as KL = acc/l1 + LSE2 - LSE1
- * with LSE_t = m_t + log l_t ("Formulazione Online", forward pass section).
+ * (two running shifts -- the page's running maxima, kept at or below them --,
+ * two running exponential sums and one accumulator of the P1-weighted logit
+ * difference), finalised as KL = acc/l1 + LSE2 - LSE1 with
+ * LSE_t = m_t + log l_t ("Formulazione Online", forward pass section).
  * The N_Q x N_K matrices P1, P2 are never written to memory.  The backward
  * pass keeps only KL, LSE1 and LSE2 per row and regenerates
  * P_t = exp(S_t - LSE_t) tile by tile ("Strategia di Ricalcolo", backward
