@@ -100,10 +100,25 @@ streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1, const void *
                                                                                   : STREAMKL_ERR_HIP;
 }
 
+namespace {
+
+// Key partitions of the query-gradient kernel for these arguments (1 = none).
+int bwd_dq_splits(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+  if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return 1;
+  if ((dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) || grad_mask < 1 || grad_mask > 3) return 1;
+  const long long bh = (long long)B * H;
+  if (bh > INT32_MAX) return 1;
+  return streamkl::bwd_dq_default_splits(int(bh), N_Q, N_K, d, dtype == STREAMKL_BF16, grad_mask);
+}
+
+}  // namespace
+
 size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype,
                                    int grad_mask) {
-  (void)B, (void)H, (void)N_Q, (void)N_K, (void)d, (void)causal, (void)dtype, (void)grad_mask;
-  return 0;  // two-kernel recompute backward: no workspace
+  (void)causal;
+  const int s = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
+  if (s <= 1) return 0;
+  return streamkl::bwd_dq_workspace_floats(B * H, N_Q, d, grad_mask, s) * sizeof(float);
 }
 
 namespace {
@@ -147,8 +162,12 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2, con
                                   dtype, grad_mask, dq1, dk1, dq2, dk2, true, true, a);
   if (s != STREAMKL_OK) return s;
   const size_t need = streamkl_bwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, grad_mask);
-  if (workspace_bytes < need || (need > 0 && !workspace)) return STREAMKL_ERR_WORKSPACE;
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
+  if (need > 0) {  // short query blocks: the query gradients by key partitions
+    a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
+    a.part = static_cast<float *>(workspace);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   // The key-gradient kernel also runs when N_Q == 0: it then writes zeros.
   if (streamkl::launch_bwd_dk(a, st) != hipSuccess) return STREAMKL_ERR_HIP;

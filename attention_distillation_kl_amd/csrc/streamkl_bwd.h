@@ -96,6 +96,12 @@ struct BwdParams {
   int nq, nk, nsb;    // nsb: stationary blocks per head
   float scale, c;     // c = scale * log2(e)
   float inv_scale;
+  // Key partitions of the query-gradient role (1 = none).  With nsplit > 1,
+  // partition s streams key tiles [s*tps, (s+1)*tps) and writes its fp32
+  // partial dQ_t (already scaled) to part_t[s][bh * N_Q + i][d]; a second
+  // kernel sums the partitions in order and converts.
+  int nsplit, tps;
+  float *part1, *part2;
 };
 
 // Per-row constants of the recompute.
@@ -133,7 +139,9 @@ constexpr bool kPairOf = BF16 && MASK == 3 && ROLE == ROLE_DK;
 template <bool BF16, int D, int MASK, int ROLE>
 using BwdCfgOf = BwdCfg<BF16, D, kPairOf<BF16, MASK, ROLE>>;
 
-template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
+// SPLIT (query-gradient role only): the workgroup folds one key partition and
+// stores fp32 partial gradients instead of the gradients themselves.
+template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(BwdCfgOf<BF16, D, MASK, ROLE>::kThreads,
                                                       BwdCfgOf<BF16, D, MASK, ROLE>::kThreads),
                           amdgpu_waves_per_eu(BwdCfgOf<BF16, D, MASK, ROLE>::kWavesPerEU,
@@ -162,9 +170,15 @@ void bwd_kernel(BwdParams p) {
   const int wrow = kPair ? wave >> 1 : wave;
   const int half = kPair ? wave & 1 : 0;
 
+  // With key partitions, the stationary blocks of one (head, partition) are
+  // consecutive, so they share the partition's tiles in one L2.
+  static_assert(!SPLIT || ROLE == ROLE_DQ, "key partitions are for the query-gradient role");
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = bid / p.nsb;
-  const int sbr = bid - bh * p.nsb;
+  const int per_bh = SPLIT ? p.nsb * p.nsplit : p.nsb;
+  const int bh = bid / per_bh;
+  const int rem = bid - bh * per_bh;
+  const int split = SPLIT ? rem / p.nsb : 0;
+  const int sbr = rem - split * p.nsb;
   // Longest rows first: for causal problems the last query blocks (ROLE_DQ)
   // and the first key blocks (ROLE_DK) see the most partners.
   const int sblk = (CAUSAL && ROLE == ROLE_DQ) ? p.nsb - 1 - sbr : sbr;
@@ -227,8 +241,12 @@ void bwd_kernel(BwdParams p) {
     if (ROLE == ROLE_DQ) t_end = min(p.nk, min(s0 + C::kBS, p.nq) + off);
     else t_begin = max(0, s0 - off);
   }
-  const int tile0 = t_begin / C::kBT;
-  const int tile1 = (t_end + C::kBT - 1) / C::kBT;
+  int tile0 = t_begin / C::kBT;
+  int tile1 = (t_end + C::kBT - 1) / C::kBT;
+  if (SPLIT) {  // this partition's share of the tiles
+    tile0 = max(tile0, split * p.tps);
+    tile1 = min(tile1, (split + 1) * p.tps);
+  }
   // ROLE_DQ: last admissible key; ROLE_DK: first admissible query.
   const int lim = ROLE == ROLE_DQ ? (CAUSAL ? min(srow + off, p.nk - 1) : p.nk - 1)
                                   : (CAUSAL ? max(srow - off, 0) : 0);
@@ -288,7 +306,7 @@ void bwd_kernel(BwdParams p) {
   }
 
   const float c = p.c;
-  const int ntiles = tile1 - tile0;
+  const int ntiles = max(tile1 - tile0, 0);
   if (ntiles > 0) {
     cload(tile0);
     issue(tile0, 0);
@@ -552,8 +570,23 @@ void bwd_kernel(BwdParams p) {
           }
         }
     };
+    // A key partition's share: scaled fp32 partial sums, d values per row.
+    auto store_part = [&](float *P, float f, const f32x16 (&A)[kMB]) {
+      float *row = P + (size_t(split) * (size_t(gridDim.x / per_bh) * p.nq) + size_t(bh) * p.nq + srow) * D;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = mb * 32 + g4 * 8 + 4 * h;
+          *reinterpret_cast<f32x4 *>(row + d0) =
+              f32x4{A[mb][4 * g4] * f, A[mb][4 * g4 + 1] * f, A[mb][4 * g4 + 2] * f, A[mb][4 * g4 + 3] * f};
+        }
+    };
     if constexpr (kPair) {
       store(half ? O2 : O1, half ? f2 : f1, acc1);
+    } else if (SPLIT) {
+      if (kG1) store_part(p.part1, f1, acc1);
+      if (kG2) store_part(p.part2, f2, acc2);
     } else {
       if (kG1) store(O1, f1, acc1);
       if (kG2) store(O2, f2, acc2);
@@ -561,8 +594,30 @@ void bwd_kernel(BwdParams p) {
   }
 }
 
+// Sum of the key partitions' partial query gradients, in partition order
+// (deterministic), converted to the gradient's element type.  One thread per
+// four consecutive values of one row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict__ part, int nsplit, size_t n4,
+                                                        char *out) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + i;
+  f32x4 acc = src[0];
+  for (int s = 1; s < nsplit; ++s) {
+    const f32x4 v = src[size_t(s) * n4];
+    acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+  }
+  if constexpr (BF16) {
+    reinterpret_cast<u32x2 *>(out)[i] = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  } else {
+    reinterpret_cast<f32x4 *>(out)[i] = acc;
+  }
+}
+
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
+  constexpr bool kCanSplit = ROLE == ROLE_DQ;
   using C = BwdCfgOf<BF16, D, MASK, ROLE>;
   BwdParams p;
   p.q1 = static_cast<const char *>(a.q1);
@@ -584,17 +639,33 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
   p.inv_scale = float(1.0 / double(a.scale));
-  const long long blocks = (long long)p.nsb * a.bh;
+  const bool split = kCanSplit && a.dq_splits > 1;
+  p.nsplit = split ? a.dq_splits : 1;
+  p.tps = (((a.nk + C::kBT - 1) / C::kBT) + p.nsplit - 1) / p.nsplit;
+  const size_t part_elems = size_t(a.bh) * a.nq * D * p.nsplit;  // per requested gradient
+  p.part1 = split ? a.part : nullptr;
+  p.part2 = split ? a.part + ((MASK & 1) ? part_elems : 0) : nullptr;
+  const long long blocks = (long long)p.nsb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-  const void *fn = reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN>);
+  const void *fn = split ? reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, kCanSplit>)
+                         : reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, false>);
   void *args[] = {&p};
   const size_t dyn = size_t(2 * C::kStage + C::kXChunks) * 16 + 2 * C::kNCst * C::kBT * 4;
   if (dyn > 65536) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
     if (e != hipSuccess) return e;
   }
-  return hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, dyn, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, dyn, stream);
+  if (e != hipSuccess || !split) return e;
+  const size_t n4 = size_t(a.bh) * a.nq * D / 4;
+  const size_t rblocks = (n4 + 255) / 256;
+  if (rblocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
+  if (MASK & 1)
+    dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks)), dim3(256), 0, stream>>>(p.part1, p.nsplit, n4, p.dq1);
+  if (MASK & 2)
+    dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks)), dim3(256), 0, stream>>>(p.part2, p.nsplit, n4, p.dq2);
+  return hipGetLastError();
 }
 
 template <int ROLE, bool BF16, int D, bool CAUSAL>

@@ -25,11 +25,18 @@ struct BwdArgs {
   float scale;
   bool causal, bf16;
   int grad_mask;  // 1: dq1/dk1, 2: dq2/dk2, 3: both
+  int dq_splits = 1;       // key partitions of the query-gradient kernel when > 1
+  float *part = nullptr;   // their fp32 partial gradients (see bwd_dq_workspace_floats)
 };
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // The library's choice of key partitions for a forward problem (1 = none).
 int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16);
+// The library's choice of key partitions for the query-gradient kernel, and
+// the fp32 workspace it then needs (splits * bh * nq * d per requested
+// gradient; 0 when splits == 1).
+int bwd_dq_default_splits(int bh, int nq, int nk, int d, bool bf16, int grad_mask);
+size_t bwd_dq_workspace_floats(int bh, int nq, int d, int grad_mask, int splits);
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
 

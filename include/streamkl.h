@@ -136,7 +136,13 @@ streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1,
 
 /*
  * streamkl_bwd_workspace_size -- bytes of device workspace streamkl_bwd needs
- * for these arguments.  The two-kernel recompute backward needs none (0).
+ * for these arguments.  0 whenever the query-gradient grid already fills the
+ * GPU.  For short query blocks (few query-row workgroups per head) the query
+ * gradients are computed by key partitions, like the split-K forward: each
+ * (query block, partition) workgroup stores its fp32 partial dq_t and a
+ * second kernel adds the partitions in a fixed order (deterministic, no
+ * atomics); the workspace then holds splits * B*H*N_Q*d floats per requested
+ * gradient, splits being the library's choice for these sizes.
  */
 size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
                                    int causal, int dtype, int grad_mask);
@@ -155,7 +161,8 @@ size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
  *   out: dq1, dk1 (required iff grad_mask has Q1K1), dq2, dk2 (iff Q2K2);
  *        pointers of unrequested gradients may be NULL and are not touched.
  *   workspace / workspace_bytes: at least streamkl_bwd_workspace_size(...)
- *        bytes (may be NULL when that is 0).
+ *        bytes, 16-byte aligned (may be NULL when that is 0), owned by the
+ *        caller; its contents are dead once the call's work has completed.
  * With N_Q == 0 the key gradients are written as zeros.
  */
 streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
@@ -172,7 +179,9 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
  * callers that schedule them separately (e.g. on two streams).  Same
  * arguments, meaning and errors as streamkl_bwd, restricted to the query
  * gradients (dq1, dq2) or to the key gradients (dk1, dk2).  streamkl_bwd is
- * exactly streamkl_bwd_dk followed by streamkl_bwd_dq on one stream.  The
+ * streamkl_bwd_dk followed by streamkl_bwd_dq on one stream, except that
+ * with a workspace (see streamkl_bwd_workspace_size) it computes the query
+ * gradients by key partitions; streamkl_bwd_dq never partitions.  The
  * page describes this split as the fallback of its fused backward when
  * atomic contention on dQ is high ("Strategia di Ricalcolo", kernel fusion
  * bullet).  Neither half needs workspace.

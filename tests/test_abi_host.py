@@ -151,9 +151,27 @@ def test_default_split_choice(lib):
         assert 1 <= s <= 1024 and (nk + 63) // 64 >= 4 * s
 
 
-def test_workspace_query_is_zero_for_two_kernel_backward(lib):
+def test_backward_workspace_query(lib):
+    # query-gradient grids that fill the GPU: no workspace
     for mask in (1, 2, 3):
         assert _lib.bwd_workspace_size(2, 32, 8192, 8192, 128, 1, _lib.BF16, mask) == 0
+    # short query blocks: key partitions, splits * B*H*N_Q*d floats per requested gradient
+    for mask, ngrad in ((1, 1), (2, 1), (3, 2)):
+        ws = _lib.bwd_workspace_size(1, 4, 64, 8192, 128, 1, _lib.BF16, mask)
+        assert ws > 0 and ws % (4 * 64 * 128 * 4 * ngrad) == 0
+        splits = ws // (4 * 64 * 128 * 4 * ngrad)
+        assert 2 <= splits <= 256 and (8192 // 64) >= 4 * splits
+    assert _lib.bwd_workspace_size(1, 4, 64, 128, 128, 1, _lib.BF16, 3) == 0   # too few key tiles
+    assert _lib.bwd_workspace_size(1, 4, 64, 8192, 96, 1, _lib.BF16, 3) == 0   # invalid sizes
+
+
+def test_bwd_rejects_short_or_misaligned_workspace(lib):
+    need = _lib.bwd_workspace_size(1, 2, 64, 8192, 128, 1, _lib.BF16, 3)
+    assert need > 0
+    kw = dict(NQ=64, NK=8192)
+    assert bwd(ws=None, wsb=0, **kw) == _lib.ERR_WORKSPACE
+    assert bwd(ws=0xC0000, wsb=need - 16, **kw) == _lib.ERR_WORKSPACE
+    assert bwd(ws=0xC0004, wsb=need, **kw) == _lib.ERR_WORKSPACE
 
 
 def test_unrequested_gradients_may_be_null(lib, no_gpu):

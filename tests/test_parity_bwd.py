@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from attention_distillation_kl_amd import WORKLOADS, make_inputs, workload_inputs
-from attention_distillation_kl_amd import ops
+from attention_distillation_kl_amd import _lib, ops
 from attention_distillation_kl_amd.inputs import upstream_grad
 from parity_util import (check_grad, check_rows, head64, log, oracle_heads, oracle_row_blocks, to64)
 
@@ -177,8 +177,10 @@ def test_autograd_function_matches_direct_calls():
 
 
 def test_bwd_halves_match_full_backward():
-    """streamkl_bwd == streamkl_bwd_dk then streamkl_bwd_dq, bit for bit."""
+    """streamkl_bwd == streamkl_bwd_dk then streamkl_bwd_dq, bit for bit, when
+    it needs no workspace (no key partitions for the query gradients)."""
     q1, k1, q2, k2 = make_inputs(1, 2, 260, 300, 128, torch.bfloat16, "student", 0.3, seed=17, device=DEV)
+    assert _lib.bwd_workspace_size(1, 2, 260, 300, 128, 1, _lib.BF16, 3) == 0
     g = upstream_grad(1, 2, 260, seed=17, device=DEV)
     kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 0.1, True)
     full = ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, 0.1, True)
