@@ -17,10 +17,12 @@
 // The page's kernel uses one fused pass with dQ atomics when the dQ buffer
 // fits in L2 and two separate kernels when contention is high.  This file is
 // the separate-kernel form: one template, two roles.
-//   ROLE_DQ: a workgroup owns 128 query rows ("stationary") and streams key
-//            tiles ("streamed") up to its causal frontier; it accumulates dQ.
-//   ROLE_DK: a workgroup owns 128 key rows and streams query tiles from its
-//            causal frontier to N_Q; it accumulates dK.
+//   ROLE_DQ: a workgroup owns 256 query rows ("stationary"; 128 for fp32
+//            with d = 128) and streams key tiles ("streamed") up to its
+//            causal frontier; it accumulates dQ.
+//   ROLE_DK: a workgroup owns 64 key rows (bf16, both gradients; else 128)
+//            and streams query tiles from its causal frontier to N_Q; it
+//            accumulates dK.
 // Both recompute S1, S2; neither needs atomics or workspace, and results are
 // bitwise deterministic.
 //
@@ -68,7 +70,9 @@ struct BwdCfg {
   using G = RowGeom<BF16, D>;
   static_assert(!PAIR || BF16, "the paired layout is for bf16");
   static constexpr bool kX1Lds = !PAIR && (BF16 || D == 64);
-  static constexpr int kWaves = (PAIR || kX1Lds) ? 8 : 4;
+  // Paired: four waves (two pairs, 64 stationary keys) and two workgroups
+  // per CU -- barriers then wait for four waves, not eight.
+  static constexpr int kWaves = PAIR ? 4 : kX1Lds ? 8 : 4;
   static constexpr int kWavesPerEU = (PAIR || kX1Lds) ? 2 : 1;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBS = 32 * (PAIR ? kWaves / 2 : kWaves);  // stationary rows per workgroup
