@@ -132,22 +132,6 @@ __device__ __forceinline__ void dma16(const void *gsrc, u32x4 *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
 }
 
-// Buffer resource for `bytes` bytes at `base` (raw, dword-addressed data;
-// accesses past `bytes` read zeros).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Asynchronous 16-byte copy from a buffer to LDS (buffer_load_dwordx4 ... lds):
-// lane L writes the 16 bytes at byte offset `voff` of the buffer to
-// lds_wave_base + 16 L.  Same contract as dma16; being a buffer rather than a
-// flat-family instruction, an outstanding copy does not force the compiler to
-// wait for every LDS read at once.
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u32x4 *lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16,
-                                          (int)voff, 0, 0, 0);
-}
-
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // Pack two fp32 values to bf16 (round to nearest even) in one dword.
