@@ -302,6 +302,23 @@ void bwd_kernel(BwdParams p) {
     }
   };
 
+  // Byte offsets of the transposing reads of the gradient products (bf16)
+  // at block 0, k-step 0, per 32-column block mb of d and row half t (see
+  // grad_bf16 below).  The swizzle depends on row bits 0-3 only, so the other
+  // blocks and k-steps (multiples of 16 rows) add a constant.
+  int trofs[kMB][2];
+  {
+    const int s16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+        const int row = 8 * t + 4 * h + (s16 >> 2);
+        trofs[mb][t] = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
+      }
+  }
+
   f32x16 acc1[kMB], acc2[kMB];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
@@ -464,8 +481,12 @@ void bwd_kernel(BwdParams p) {
           u32x4 a;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
+            // The paired kernel schedules better with the offset formed per
+            // read; the others keep fewer address registers with the hoisted
+            // offsets (measured).
             const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
-            const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
+            const int byte = kPair ? (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2
+                                   : trofs[mb][t] + (sb * 32 + 16 * ks) * G::kRowBytes;
             const u32x2 v = read_tr(yb + byte);
             a[2 * t] = v[0];
             a[2 * t + 1] = v[1];
