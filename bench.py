@@ -90,7 +90,7 @@ def copy_probe(nbytes):
 def cpu_baseline(w, q1, k1, q2, k2, target_s):
     """Time the fp64 oracle (as it stands) on the last query rows of head 0.
 
-    The sample grows until one run of it takes at least a third of
+    The sample grows until one run of it takes at least two thirds of
     ``target_s`` seconds; that run is the one reported.  The sample is the
     forward + backward of the last R query rows of head 0 (for causal
     workloads the longest rows); its credited work is 16 d flops per
@@ -115,11 +115,11 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s):
 
     rows = min(w.NQ, 32)
     run(rows)                          # threads and pages warm
-    while True:                        # grow the sample until it takes a third of the target
+    while True:                        # grow the sample until it takes two thirds of the target
         dt = run(rows)
-        if dt >= target_s / 3 or rows >= w.NQ:
+        if dt >= target_s * 2 / 3 or rows >= w.NQ:
             break
-        rows = min(w.NQ, int(rows * min(16.0, max(2.0, target_s / max(dt, 1e-3)))))
+        rows = min(w.NQ, int(rows * min(16.0, max(1.5, target_s / max(dt, 1e-3)))))
     fl = credited(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"fp64 oracle, forward+backward of the last {rows} query rows of head 0 "
