@@ -140,9 +140,15 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     const int r0 = wq0 + 32 * j;
-    my_last[j] = CAUSAL ? min(r0 + col + off, p.nk - 1) : p.nk - 1;
-    blk_lo[j] = CAUSAL ? min(r0 + off, p.nk - 1) : p.nk - 1;
-    blk_hi[j] = CAUSAL ? min(r0 + 31 + off, p.nk - 1) : p.nk - 1;
+    // Without the mask every row ends at the last key: the same formula with
+    // offset N_K (in 64 bits) gives N_K - 1.  Writing the constant instead
+    // lets the compiler specialise the loop on it, and that instantiation
+    // then spills 36 registers.
+    const long long eo = CAUSAL ? off : p.nk;
+    const long long last = p.nk - 1;
+    my_last[j] = int(min((long long)(r0 + col) + eo, last));
+    blk_lo[j] = int(min((long long)r0 + eo, last));
+    blk_hi[j] = int(min((long long)(r0 + 31) + eo, last));
   }
   const int w_hi = blk_hi[NQB - 1];
 

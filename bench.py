@@ -72,6 +72,11 @@ def parse():
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="context-length sweep instead of the headline: N = 4K..--sweep-max, "
+                         "forward and each backward configuration, causal and not; one JSON line per N")
+    ap.add_argument("--sweep-max", type=int, default=524288)
+    ap.add_argument("--sweep-heads", type=int, default=32)
     return ap.parse_args()
 
 
@@ -126,10 +131,79 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s):
                       f"({fl / 1e12:.3f} TFLOP credited, {dt:.1f} s)"}
 
 
+def sweep(args):
+    """Latency and memory against context length, on the axes of the page's
+    results ("Risultati Sperimentali": 4K to 512K tokens; forward latency,
+    causal and not; backward latency of Configuration 1 and Configuration 2;
+    memory footprint).  B = 1, H = --sweep-heads, d = 128, bf16, student =
+    teacher + 0.2 N(0,1).  For each N and mask the times are HIP events around
+    one library call on the current stream (median of the timed calls), and
+    `extra_hbm_bytes` is the peak device memory of the call minus its inputs
+    and outputs: the workspace and anything else it needed."""
+    import torch
+    from attention_distillation_kl_amd import make_inputs, ops, _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H, d = args.sweep_heads, 128
+    n = 4096
+    while n <= args.sweep_max:
+        q1, k1, q2, k2 = make_inputs(1, H, n, n, d, torch.bfloat16, "student", 0.2,
+                                     seed=2000 + n.bit_length(), device=dev)
+        reps = 3 if n <= 65536 else 1
+        row = {"N": n, "B": 1, "H": H, "d": d, "dtype": "bf16",
+               "input_bytes": 4 * q1.numel() * q1.element_size()}
+        for causal in (True, False):
+            tag = "causal" if causal else "noncausal"
+
+            def timed(fn, out_bytes):
+                fn()                          # warm-up (and the result the backward needs)
+                torch.cuda.synchronize()
+                torch.cuda.reset_peak_memory_stats(dev)
+                base = torch.cuda.memory_allocated(dev)
+                ms = []
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    r = fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms.append(e0.elapsed_time(e1))
+                    del r
+                extra = torch.cuda.max_memory_allocated(dev) - base - out_bytes
+                return sorted(ms)[len(ms) // 2], max(0, extra)
+
+            fwd_out = 3 * H * n * 4
+            t, x = timed(lambda: ops.streamkl_fwd(q1, k1, q2, k2, None, causal), fwd_out)
+            kl, lse1, lse2 = ops.streamkl_fwd(q1, k1, q2, k2, None, causal)
+            fl = 4.0 * H * n * n * d * (0.5 if causal else 1.0)
+            row[f"fwd_ms_{tag}"] = round(t, 4)
+            row[f"fwd_tflops_{tag}"] = round(fl / (t * 1e-3) / 1e12, 1)
+            row[f"fwd_extra_hbm_bytes_{tag}"] = x
+            for cfg, mask in (("config1", _lib.GRAD_Q2K2), ("config2", _lib.GRAD_Q1K1)):
+                grad_out = 2 * q1.numel() * q1.element_size()
+                t, x = timed(lambda: ops.streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, None, None, causal, mask),
+                             grad_out)
+                row[f"bwd_{cfg}_ms_{tag}"] = round(t, 4)
+                row[f"bwd_{cfg}_extra_hbm_bytes_{tag}"] = x
+            del kl, lse1, lse2
+            log(f"bench: sweep N={n} {tag} done")
+        print(json.dumps(row), flush=True)
+        del q1, k1, q2, k2
+        torch.cuda.empty_cache()
+        n *= 2
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        sweep(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

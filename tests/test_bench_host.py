@@ -32,6 +32,7 @@ def test_profiling_options_exist():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "--copy-probe" in r.stdout and "--no-cpu-baseline" in r.stdout
+    assert "--sweep" in r.stdout
 
 
 def test_recorded_traffic_lines_are_well_formed():
