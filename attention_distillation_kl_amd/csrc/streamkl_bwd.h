@@ -23,8 +23,10 @@
 //   ROLE_DK: a workgroup owns 64 key rows (bf16, both gradients; else 128)
 //            and streams query tiles from its causal frontier to N_Q; it
 //            accumulates dK.
-// Both recompute S1, S2; neither needs atomics or workspace, and results are
-// bitwise deterministic.
+// Both recompute S1, S2; neither needs atomics, and results are bitwise
+// deterministic.  For short query blocks the query-gradient role can also run
+// by key partitions (SPLIT below): partial sums in a caller's workspace, added
+// in a fixed order by dq_reduce_kernel.
 //
 // Per 32-row block of a streamed tile, each wave:
 //   1. S_t^T block (32 streamed x 32 stationary) = Y_t X_t^T with the
