@@ -1,0 +1,49 @@
+"""Device memory of the library's calls: nothing beyond inputs, outputs and
+the workspace its query functions declare.
+
+The page's memory claim ("Risultati Sperimentali": a flat footprint at every
+context length, against the quadratic one of materialising implementations)
+holds here by construction -- the library allocates nothing -- and this test
+checks it through the benchmark's own sweep: for each call, the peak device
+memory beyond the call's inputs and outputs must equal the workspace that
+streamkl_fwd_workspace_size / streamkl_bwd_workspace_size report (as torch
+rounds allocations, to 512 bytes).
+"""
+import argparse
+import json
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def _round512(n):
+    return (n + 511) // 512 * 512
+
+
+def test_sweep_needs_only_the_declared_workspace(capsys):
+    import bench
+    from attention_distillation_kl_amd import _lib
+
+    H, d = 2, 128
+    bench.sweep(argparse.Namespace(sweep_max=8192, sweep_heads=H))
+    rows = [json.loads(line) for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    assert [r["N"] for r in rows] == [4096, 8192]
+    for r in rows:
+        n = r["N"]
+        assert r["input_bytes"] == 4 * H * n * d * 2
+        for causal in (True, False):
+            tag = "causal" if causal else "noncausal"
+            s = _lib.fwd_splits(1, H, n, n, d, int(causal), _lib.BF16)
+            ws = _lib.fwd_workspace_size(1, H, n, n, d, int(causal), _lib.BF16, s) if s > 1 else 0
+            assert r[f"fwd_extra_hbm_bytes_{tag}"] == _round512(ws), (n, tag)
+            for cfg, mask in (("config1", _lib.GRAD_Q2K2), ("config2", _lib.GRAD_Q1K1)):
+                ws = _lib.bwd_workspace_size(1, H, n, n, d, int(causal), _lib.BF16, mask)
+                assert r[f"bwd_{cfg}_extra_hbm_bytes_{tag}"] == _round512(ws), (n, tag, cfg)
+            assert r[f"fwd_ms_{tag}"] > 0 and r[f"bwd_config1_ms_{tag}"] > 0
+    # At these sizes (2 heads) both the split-K forward and the partitioned
+    # backward are chosen, so the workspace paths are the ones measured.
+    assert _lib.fwd_splits(1, H, 4096, 4096, d, 1, _lib.BF16) > 1
+    assert _lib.bwd_workspace_size(1, H, 4096, 4096, d, 1, _lib.BF16, 3) > 0
