@@ -169,7 +169,7 @@ void bwd_kernel(BwdParams p) {
   __shared__ u32x4 xch[kPair ? C::kWaves * 128 : 1];          // pairs' exchange slots
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   // The wave's 32 stationary rows within the workgroup and, in a pair, the
   // streamed block it scores and the gradient it accumulates (0: teacher).
@@ -262,17 +262,31 @@ void bwd_kernel(BwdParams p) {
   // Lane L of wave w fills chunk position i*256 + 64w + L; the global side
   // picks the (row, logical chunk) stored there (the swizzle is an XOR, its
   // own inverse).  Rows past the end repeat the last row; they are masked.
+  // Full tiles take 32-bit offsets from the head's base: one per copy, a
+  // constant apart; the last tile clamps each row.
   auto issue = [&](int tile, int stage) {
+    u32x4 *wbase = (stage ? ystage1 : ystage0) + wave * 64;
+    if ((tile + 1) * C::kBT <= nt) {
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int pos = i * C::kThreads + tid;
-      const int row = pos / G::kChunks;
-      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
-      const int r = min(tile * C::kBT + row, nt - 1);
-      const size_t o = size_t(r) * G::kRowBytes + ch * 16;
-      u32x4 *base = (stage ? ystage1 : ystage0) + i * C::kThreads + wave * 64;
-      dma16(Y1 + o, base);
-      dma16(Y2 + o, base + C::kOffY2);
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int pos = i * C::kThreads + tid;
+        const int row = pos / G::kChunks;
+        const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+        const uint32_t o = uint32_t(tile * C::kBT + row) * G::kRowBytes + uint32_t(ch * 16);
+        dma16(Y1 + o, wbase + i * C::kThreads);
+        dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int pos = i * C::kThreads + tid;
+        const int row = pos / G::kChunks;
+        const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+        const int r = min(tile * C::kBT + row, nt - 1);
+        const size_t o = size_t(r) * G::kRowBytes + ch * 16;
+        dma16(Y1 + o, wbase + i * C::kThreads);
+        dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
+      }
     }
   };
   // ROLE_DK: the next tile's per-row inputs, loaded while the current tile is
