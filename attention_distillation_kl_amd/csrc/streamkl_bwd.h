@@ -262,11 +262,13 @@ void bwd_kernel(BwdParams p) {
   // Lane L of wave w fills chunk position i*256 + 64w + L; the global side
   // picks the (row, logical chunk) stored there (the swizzle is an XOR, its
   // own inverse).  Rows past the end repeat the last row; they are masked.
-  // Full tiles take 32-bit offsets from the head's base: one per copy, a
-  // constant apart; the last tile clamps each row.
+  // Full tiles take 32-bit offsets from the head's base (where a head's rows
+  // span fewer than 2^32 bytes): one per copy, a constant apart.  The last
+  // tile, and heads of 4 GiB or more, use 64-bit offsets and clamp each row.
+  const bool off32 = size_t(nt) * G::kRowBytes <= size_t(0xFFFFFFFFu);
   auto issue = [&](int tile, int stage) {
     u32x4 *wbase = (stage ? ystage1 : ystage0) + wave * 64;
-    if ((tile + 1) * C::kBT <= nt) {
+    if (off32 && (tile + 1) * C::kBT <= nt) {
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i) {
         const int pos = i * C::kThreads + tid;
