@@ -463,14 +463,17 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16) {
-  // Partitions of the key dimension so that the grid holds about four
-  // workgroups per CU (two resident, two queued), each partition keeping at
-  // least four key tiles.  Grids that are already that large are not split.
+  // Partitions of the key dimension so that the grid is one round of
+  // resident workgroups (two per CU), each partition keeping at least four
+  // key tiles.  Grids that are already that large are not split.  (Measured:
+  // a second round of half-size partitions costs up to 20% more for short
+  // query blocks, since each workgroup also pays its fragment loads and
+  // state stores.)
   const bool nqb2 = bf16 || d == 64;
   const int kbq = nqb2 ? 256 : 128, kbk = bf16 ? 64 : 32;
   const long long nwg = (long long)bh * ((nq + kbq - 1) / kbq);
   if (nwg <= 0) return 1;
-  constexpr long long kTarget = 1024;
+  constexpr long long kTarget = 2 * 256;
   if (nwg >= kTarget) return 1;
   const long long tiles = (nk + kbk - 1) / kbk;
   long long s = (kTarget + nwg - 1) / nwg;
