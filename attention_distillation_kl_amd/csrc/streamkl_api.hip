@@ -64,12 +64,11 @@ streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2, con
 }
 
 int streamkl_fwd_splits(int B, int H, int N_Q, int N_K, int d, int causal, int dtype) {
-  (void)causal;
   if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return 1;
   if (dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) return 1;
   const long long bh = (long long)B * H;
   if (bh > INT32_MAX) return 1;
-  return streamkl::fwd_default_splits(int(bh), N_Q, N_K, d, dtype == STREAMKL_BF16);
+  return streamkl::fwd_default_splits(int(bh), N_Q, N_K, d, dtype == STREAMKL_BF16, causal != 0);
 }
 
 size_t streamkl_fwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype, int splits) {

@@ -462,22 +462,27 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16) {
-  // Partitions of the key dimension so that the grid is one round of
+int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal) {
+  // Partitions of the key dimension so that the grid fills one round of
   // resident workgroups (two per CU), each partition keeping at least four
-  // key tiles.  Grids that are already that large are not split.  (Measured:
-  // a second round of half-size partitions costs up to 20% more for short
-  // query blocks, since each workgroup also pays its fragment loads and
-  // state stores.)
+  // key tiles.  (Measured: a second round of half-size partitions costs up
+  // to 20% more for short query blocks, since each workgroup also pays its
+  // fragment loads and state stores.)  Causal problems with N_Q > N_K / 2
+  // are uneven: the causal triangle makes the query blocks' work differ up
+  // to N_Q / 256 fold, so they also get partitions of at least 16 tiles for
+  // about four rounds, which lets the workgroups balance (measured 5-17%
+  // faster at 4K-8K tokens).  The larger of the two counts is taken.
   const bool nqb2 = bf16 || d == 64;
   const int kbq = nqb2 ? 256 : 128, kbk = bf16 ? 64 : 32;
   const long long nwg = (long long)bh * ((nq + kbq - 1) / kbq);
   if (nwg <= 0) return 1;
-  constexpr long long kTarget = 2 * 256;
-  if (nwg >= kTarget) return 1;
   const long long tiles = (nk + kbk - 1) / kbk;
-  long long s = (kTarget + nwg - 1) / nwg;
-  s = std::min(s, std::max(1LL, tiles / 4));
+  auto count = [&](long long target, long long min_tiles) {
+    if (nwg >= target) return 1LL;
+    return std::min((target + nwg - 1) / nwg, std::max(1LL, tiles / min_tiles));
+  };
+  long long s = count(2 * 256, 4);
+  if (causal && 2LL * nq > nk) s = std::max(s, count(8 * 256, 16));
   return int(std::min(s, 256LL));
 }
 

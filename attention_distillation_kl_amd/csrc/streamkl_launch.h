@@ -31,7 +31,7 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // The library's choice of key partitions for a forward problem (1 = none).
-int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16);
+int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal);
 // The library's choice of key partitions for the query-gradient kernel, and
 // the fp32 workspace it then needs (splits * bh * nq * d per requested
 // gradient; 0 when splits == 1).

@@ -92,8 +92,11 @@ streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2,
  * streamkl_fwd_splits -- the library's choice of key partitions for
  * streamkl_fwd_splitk on this problem: enough that short query blocks (few
  * workgroups per head, e.g. N_Q = 1 decoding or 2K queries over 64K keys)
- * still fill every compute unit, at least four key tiles per partition, and
- * 1 (no split) when the unsplit grid already fills the GPU.  Invalid sizes
+ * still fill every compute unit once, at least four key tiles per
+ * partition, and 1 (no split) when the unsplit grid already fills the GPU.
+ * Causal problems with N_Q > N_K / 2, whose query blocks carry very
+ * different amounts of work, get about four times as many workgroups (at
+ * least 16 key tiles per partition) so that they balance.  Invalid sizes
  * give 1.
  */
 int streamkl_fwd_splits(int B, int H, int N_Q, int N_K, int d, int causal, int dtype);
