@@ -159,9 +159,11 @@ void bwd_kernel(BwdParams p) {
   constexpr bool kG1 = (MASK & 1) != 0;
   constexpr bool kG2 = (MASK & 2) != 0;
   constexpr int kMB = D / 32;  // 32-row blocks of d in the gradient accumulators
-  // LDS, one array per role so that the compiler can tell that reading one
-  // stage (or the row constants, the stationary tile, the exchange slots)
-  // need not wait for the copies in flight into the other stage.
+  // LDS: the stages, the stationary tile and the row constants at fixed
+  // offsets of one dynamic array, the pairs' exchange slots in a static one.
+  // From the constant offsets the compiler can tell that reading one stage
+  // (or the constants, the stationary tile, the slots) need not wait for the
+  // copies in flight into the other stage.
   extern __shared__ u32x4 lds[];
   u32x4 *ystage0 = lds, *ystage1 = lds + C::kStage;
   u32x4 *xtile = lds + 2 * C::kStage;
@@ -259,7 +261,7 @@ void bwd_kernel(BwdParams p) {
 
   // ------------------------------------------------------------ staging
   // Streamed tile `tile` -> LDS buffer `stage` by direct global->LDS copies.
-  // Lane L of wave w fills chunk position i*256 + 64w + L; the global side
+  // Lane L of wave w fills chunk position i*threads + 64w + L; the global side
   // picks the (row, logical chunk) stored there (the swizzle is an XOR, its
   // own inverse).  Rows past the end repeat the last row; they are masked.
   // Full tiles take 32-bit offsets from the head's base (where a head's rows
@@ -353,9 +355,6 @@ void bwd_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // One streamed tile.  `stage_c` is the LDS buffer as a compile-time
-  // constant, so every LDS address below is a loop-invariant lane offset plus
-  // an immediate; the loop is unrolled by two to alternate the buffers.
   // e1/e2 of one 32-row block in the form the gradient product consumes:
   // packed bf16 B operands for the two 16-row k-steps, or fp32 values.
   struct EBlock {
