@@ -71,7 +71,7 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h32k")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -80,12 +80,51 @@ def parse():
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates HBM byte counters)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the GPU clock under load after the timed steps")
     ap.add_argument("--sweep", action="store_true",
                     help="context-length sweep instead of the headline: N = 4K..--sweep-max, "
                          "forward and each backward configuration, causal and not; one JSON line per N")
     ap.add_argument("--sweep-max", type=int, default=524288)
     ap.add_argument("--sweep-heads", type=int, default=32)
     return ap.parse_args()
+
+
+def sample_clock():
+    """Current graphics clock of GPU 0 (MHz, mean over its XCDs) from
+    `amd-smi metric --clock --json`, else `rocm-smi --showclocks --json`;
+    None when neither answers."""
+    import re
+    import subprocess
+
+    def first_json(text):
+        starts = [i for i in (text.find("["), text.find("{")) if i >= 0]
+        return json.JSONDecoder().raw_decode(text[min(starts):])[0]
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json", "-g", "0"], capture_output=True,
+                           text=True, timeout=30)
+        data = first_json(r.stdout)
+        if isinstance(data, dict) and "gpu_data" in data:
+            data = data["gpu_data"]
+        gpu = data[0] if isinstance(data, list) else data
+        clocks = gpu.get("clock", gpu)
+        vals = [v["clk"]["value"] for k, v in clocks.items() if k.startswith("gfx") and isinstance(v, dict)]
+        vals = [float(v) for v in vals if isinstance(v, (int, float))]
+        if vals:
+            return {"sclk_mhz": round(sum(vals) / len(vals), 1), "xcds": len(vals), "source": "amd-smi metric --clock"}
+    except Exception:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = first_json(r.stdout)
+        card = next(iter(data.values()))
+        m = re.search(r"(\d+)\s*Mhz", card.get("sclk clock speed:", ""), re.I)
+        if m:
+            return {"sclk_mhz": float(m.group(1)), "xcds": None, "source": "rocm-smi --showclocks"}
+    except Exception:
+        pass
+    return None
 
 
 def copy_probe(nbytes):
@@ -265,7 +304,8 @@ def main():
     log(f"bench: {args.steps} timed steps done in {wall:.3f} s")
 
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    step_ms = sum(e[0].elapsed_time(e[nev - 1]) for e in events) / args.steps
+    step_ev = sorted(e[0].elapsed_time(e[nev - 1]) for e in events)
+    step_ms = sum(step_ev) / args.steps
     kern = {"fwd": fwd_ms}
     if do_bwd:
         kern["bwd_dk"] = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
@@ -287,6 +327,22 @@ def main():
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, dom),
             "flops_per_launch": per_launch[dom], "avg_launch_ms": round(kern[dom], 4)}
+
+    # The graphics clock, sampled while untimed steps keep the GPU busy (the
+    # clock drops within milliseconds once the GPU idles).
+    clock = None
+    if not args.no_clock:
+        import threading
+        got = {}
+        th = threading.Thread(target=lambda: got.update(c=sample_clock()))
+        th.start()
+        while th.is_alive():
+            step()
+            torch.cuda.synchronize()
+        th.join()
+        clock = got.get("c")
+        if clock is not None:
+            clock["published_peak_mhz"] = 2400
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -314,6 +370,9 @@ def main():
         "pct_peak_fwd": round(100 * fwd_tf / peak, 2),
         "pct_peak_fwdbwd": round(100 * value / peak, 2),
         "event_ms_per_step": round(step_ms, 4),
+        "event_ms_median": round(step_ev[len(step_ev) // 2], 4),
+        "event_ms_min": round(step_ev[0], 4),
+        "observed_clock": clock,
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
