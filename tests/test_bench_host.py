@@ -41,3 +41,50 @@ def test_recorded_traffic_lines_are_well_formed():
     for kernel in ("fwd", "bwd_dk", "bwd_dq"):
         t = bench.recorded_traffic("h32k", kernel)
         assert t is None or t > 1e9  # present only while the kernel's sources are unchanged
+
+
+def test_clock_sampling_parses_amd_smi_then_rocm_smi(monkeypatch):
+    """The graphics clock under load: amd-smi's per-XCD clocks (averaged),
+    with text around the JSON; rocm-smi's single reading when amd-smi fails;
+    None when neither answers."""
+    import subprocess
+    import types
+    sys.path.insert(0, ROOT)
+    import bench
+
+    amd = ('WARNING: something\n{"gpu_data": [{"gpu": 0, "clock": {'
+           '"gfx_0": {"clk": {"value": 2000, "unit": "MHz"}}, "gfx_1": {"clk": {"value": 1900, "unit": "MHz"}}, '
+           '"mem_0": {"clk": {"value": 2000, "unit": "MHz"}}}}]}\n')
+    rocm = '{"card0": {"sclk clock speed:": "(1960Mhz)", "sclk clock level:": "S"}}\nWARNING: x\n'
+    answers = {}
+
+    def fake_run(cmd, **kw):
+        out = answers.get(cmd[0])
+        if out is None:
+            raise FileNotFoundError(cmd[0])
+        return types.SimpleNamespace(stdout=out, returncode=0)
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    answers.update({"amd-smi": amd, "rocm-smi": rocm})
+    c = bench.sample_clock()
+    assert c["sclk_mhz"] == 1950.0 and c["xcds"] == 2 and c["source"].startswith("amd-smi")
+    answers.pop("amd-smi")
+    c = bench.sample_clock()
+    assert c["sclk_mhz"] == 1960.0 and c["source"].startswith("rocm-smi")
+    answers.clear()
+    assert bench.sample_clock() is None
+
+
+def test_kernel_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "probe", ["k.hip"])
+    src.write_text("int f(int x) {\n  return x + 1;  // add one\n}\n")
+    h0 = bench.kernel_hash("probe")
+    src.write_text("/* a block\n comment */ int f(int x) {   return x + 1; }\n// trailing\n")
+    assert bench.kernel_hash("probe") == h0
+    src.write_text("int f(int x) {\n  return x + 2;\n}\n")
+    assert bench.kernel_hash("probe") != h0
