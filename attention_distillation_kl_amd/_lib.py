@@ -14,7 +14,7 @@ F32, BF16 = 0, 1
 GRAD_Q1K1, GRAD_Q2K2, GRAD_ALL = 1, 2, 3
 
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splits", "streamkl_fwd_workspace_size", "streamkl_fwd_splitk",
-           "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dk",
+           "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dq_ws", "streamkl_bwd_dk",
            "streamkl_bwd_workspace_size", "streamkl_status_str", "streamkl_abi_version")
 
 
@@ -55,6 +55,9 @@ def load(path: str = LIB_PATH):
         fn.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
                        _f, _i, _i, _i, _vp, _vp, _vp]
         fn.restype = _i
+    lib.streamkl_bwd_dq_ws.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
+                                       _f, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
+    lib.streamkl_bwd_dq_ws.restype = _i
     lib.streamkl_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
     lib.streamkl_bwd_workspace_size.restype = _sz
     lib.streamkl_status_str.argtypes = [_i]
@@ -108,6 +111,13 @@ def bwd_half(which, q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale,
     fn = getattr(load(), f"streamkl_bwd_{which}")
     return fn(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
               out1, out2, stream)
+
+
+def bwd_dq_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
+              dq1, dq2, workspace, workspace_bytes, stream):
+    """streamkl_bwd_dq_ws: the query-gradient half with the backward's workspace."""
+    return load().streamkl_bwd_dq_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal,
+                                     dtype, grad_mask, dq1, dq2, workspace, workspace_bytes, stream)
 
 
 def bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask):

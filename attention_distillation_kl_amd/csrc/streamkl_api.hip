@@ -149,6 +149,20 @@ streamkl_status prepare_bwd(const void *q1, const void *k1, const void *q2, cons
 
 bool bwd_is_noop(int B, int H, int N_Q, int N_K) { return (long long)B * H == 0 || (N_Q == 0 && N_K == 0); }
 
+// Checks the caller's workspace against streamkl_bwd_workspace_size and, where
+// that size is not zero (short query blocks), switches the query-gradient
+// kernel to key partitions whose partial sums go to the workspace.
+streamkl_status attach_dq_workspace(streamkl::BwdArgs &a, int B, int H, int N_Q, int N_K, int d, int causal,
+                                    int dtype, int grad_mask, void *workspace, size_t workspace_bytes) {
+  const size_t need = streamkl_bwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, grad_mask);
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
+  if (need > 0) {
+    a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
+    a.part = static_cast<float *>(workspace);
+  }
+  return STREAMKL_OK;
+}
+
 }  // namespace
 
 streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2, const void *k2,
@@ -160,13 +174,9 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2, con
   streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
                                   dtype, grad_mask, dq1, dk1, dq2, dk2, true, true, a);
   if (s != STREAMKL_OK) return s;
-  const size_t need = streamkl_bwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, grad_mask);
-  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
+  s = attach_dq_workspace(a, B, H, N_Q, N_K, d, causal, dtype, grad_mask, workspace, workspace_bytes);
+  if (s != STREAMKL_OK) return s;
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
-  if (need > 0) {  // short query blocks: the query gradients by key partitions
-    a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
-    a.part = static_cast<float *>(workspace);
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   // The key-gradient kernel also runs when N_Q == 0: it then writes zeros.
   if (streamkl::launch_bwd_dk(a, st) != hipSuccess) return STREAMKL_ERR_HIP;
@@ -181,6 +191,22 @@ streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2, 
   streamkl::BwdArgs a;
   streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
                                   dtype, grad_mask, dq1, nullptr, dq2, nullptr, true, false, a);
+  if (s != STREAMKL_OK) return s;
+  if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
+  return streamkl::launch_bwd_dq(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
+                                                                                     : STREAMKL_ERR_HIP;
+}
+
+streamkl_status streamkl_bwd_dq_ws(const void *q1, const void *k1, const void *q2, const void *k2,
+                                   const float *kl, const float *lse1, const float *lse2, const float *dkl,
+                                   int B, int H, int N_Q, int N_K, int d, float scale, int causal, int dtype,
+                                   int grad_mask, void *dq1, void *dq2, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  streamkl::BwdArgs a;
+  streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
+                                  dtype, grad_mask, dq1, nullptr, dq2, nullptr, true, false, a);
+  if (s != STREAMKL_OK) return s;
+  s = attach_dq_workspace(a, B, H, N_Q, N_K, d, causal, dtype, grad_mask, workspace, workspace_bytes);
   if (s != STREAMKL_OK) return s;
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
   return streamkl::launch_bwd_dq(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK

@@ -140,42 +140,59 @@ def copy_probe(nbytes):
 
 
 def cpu_baseline(w, q1, k1, q2, k2, target_s):
-    """Time the fp64 oracle (as it stands) on the last query rows of head 0.
+    """Time the fp64 oracle (as it stands) on a sample of the workload.
 
-    The sample grows until one run of it takes at least two thirds of
-    ``target_s`` seconds; that run is the one reported.  The sample is the
-    forward + backward of the last R query rows of head 0 (for causal
-    workloads the longest rows); its credited work is 16 d flops per
-    admissible (query, key) pair, the same count as the GPU's fwd+bwd
-    figure."""
+    The sample is the last R query rows of head 0 (for causal workloads the
+    longest rows), then -- once R covers the head -- whole heads 0..n-1; it
+    grows until one run of it takes at least two thirds of ``target_s``
+    seconds, and that run is the one reported.  The oracle computes what the
+    workload's timed step computes (forward + backward, or the forward
+    alone), credited with the GPU figure's count per admissible (query, key)
+    pair: 16 d flops for forward + backward, 4 d for the forward."""
     import numpy as np
     import torch
     import oracle
 
-    c = [t[0, 0].to("cpu", torch.float64).numpy() for t in (q1, k1, q2, k2)]
+    grads = w.passes == "fwd+bwd"
+    per_pair = (16.0 if grads else 4.0) * w.d
     off = w.NK - w.NQ
+    nheads = w.B * w.H
+    cache = {}
+
+    def head(hh):
+        if hh not in cache:
+            b, h = divmod(hh, w.H)
+            cache[hh] = [t[b, h].to("cpu", torch.float64).numpy() for t in (q1, k1, q2, k2)]
+        return cache[hh]
 
     def credited(rows):
         rb = w.NQ - rows
         keys = np.array([min(w.NK, i + off + 1) if w.causal else w.NK for i in range(rb, w.NQ)], dtype=np.float64)
-        return 16.0 * w.d * keys.sum()
+        return per_pair * keys.sum()
 
-    def run(rows):
+    def run(rows, nh):
+        hs = [head(hh) for hh in range(nh)]   # conversions are not timed
         t0 = time.perf_counter()
-        oracle.head(*c, w.scale, w.causal, rows=(w.NQ - rows, w.NQ), grads=True)
+        for c in hs:
+            oracle.head(*c, w.scale, w.causal, rows=(w.NQ - rows, w.NQ), grads=grads)
         return time.perf_counter() - t0
 
-    rows = min(w.NQ, 32)
-    run(rows)                          # threads and pages warm
+    rows, nh = min(w.NQ, 32), 1
+    run(rows, nh)                      # threads and pages warm
     while True:                        # grow the sample until it takes two thirds of the target
-        dt = run(rows)
-        if dt >= target_s * 2 / 3 or rows >= w.NQ:
+        dt = run(rows, nh)
+        if dt >= target_s * 2 / 3 or (rows >= w.NQ and nh >= nheads):
             break
-        rows = min(w.NQ, int(rows * min(16.0, max(1.5, target_s / max(dt, 1e-3)))))
-    fl = credited(rows)
+        f = min(16.0, max(1.5, target_s / max(dt, 1e-3)))
+        if rows < w.NQ:
+            rows = min(w.NQ, int(rows * f))
+        else:
+            nh = min(nheads, int(math.ceil(nh * f)))
+    fl = credited(rows) * nh
+    what = "forward+backward" if grads else "forward"
+    where = f"the last {rows} query rows of head 0" if nh == 1 else f"all {rows} query rows of heads 0..{nh - 1}"
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"fp64 oracle, forward+backward of the last {rows} query rows of head 0 "
-                      f"({fl / 1e12:.3f} TFLOP credited, {dt:.1f} s)"}
+            "sample": f"fp64 oracle, {what} of {where} ({fl / 1e12:.3f} TFLOP credited, {dt:.1f} s)"}
 
 
 def sweep(args):
@@ -273,6 +290,9 @@ def main():
     dq = (torch.empty_like(q1), torch.empty_like(q2))
     dk = (torch.empty_like(k1), torch.empty_like(k2))
     do_bwd = w.passes == "fwd+bwd"
+    # The backward's workspace (short query blocks only), allocated once: the
+    # query half then takes the key-partitioned path, as streamkl_bwd does.
+    ws = ops.streamkl_bwd_workspace(q1, k1, w.causal) if do_bwd else None
 
     def step(ev=None):
         if ev is not None:
@@ -284,7 +304,8 @@ def main():
             ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dk)
             if ev is not None:
                 ev[2].record()
-            ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dq)
+            ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dq,
+                                  workspace=ws)
             if ev is not None:
                 ev[3].record()
 

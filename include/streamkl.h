@@ -181,13 +181,20 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
  * streamkl_bwd_dq / streamkl_bwd_dk -- the two halves of streamkl_bwd, for
  * callers that schedule them separately (e.g. on two streams).  Same
  * arguments, meaning and errors as streamkl_bwd, restricted to the query
- * gradients (dq1, dq2) or to the key gradients (dk1, dk2).  streamkl_bwd is
- * streamkl_bwd_dk followed by streamkl_bwd_dq on one stream, except that
- * with a workspace (see streamkl_bwd_workspace_size) it computes the query
- * gradients by key partitions; streamkl_bwd_dq never partitions.  The
- * page describes this split as the fallback of its fused backward when
- * atomic contention on dQ is high ("Strategia di Ricalcolo", kernel fusion
- * bullet).  Neither half needs workspace.
+ * gradients (dq1, dq2) or to the key gradients (dk1, dk2).  Neither takes a
+ * workspace: streamkl_bwd_dq never partitions the keys.  The page describes
+ * this split as the fallback of its fused backward when atomic contention on
+ * dQ is high ("Strategia di Ricalcolo", kernel fusion bullet).
+ *
+ * streamkl_bwd_dq_ws -- the query-gradient half with streamkl_bwd's
+ * workspace: workspace / workspace_bytes as for streamkl_bwd (at least
+ * streamkl_bwd_workspace_size(...) bytes for the same sizes and grad_mask,
+ * 16-byte aligned, caller-owned, STREAMKL_ERR_WORKSPACE otherwise).  Where
+ * that size is not zero (short query blocks) the query gradients are
+ * computed by key partitions, partial sums in the workspace, added in a
+ * fixed order; otherwise it is streamkl_bwd_dq.  streamkl_bwd is
+ * streamkl_bwd_dk followed by streamkl_bwd_dq_ws on one stream, with
+ * bitwise the same results.
  */
 streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2,
                                 const void *k2, const float *kl,
@@ -196,6 +203,14 @@ streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2,
                                 int N_K, int d, float scale, int causal,
                                 int dtype, int grad_mask, void *dq1, void *dq2,
                                 void *stream);
+streamkl_status streamkl_bwd_dq_ws(const void *q1, const void *k1,
+                                   const void *q2, const void *k2,
+                                   const float *kl, const float *lse1,
+                                   const float *lse2, const float *dkl, int B,
+                                   int H, int N_Q, int N_K, int d, float scale,
+                                   int causal, int dtype, int grad_mask,
+                                   void *dq1, void *dq2, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2,
                                 const void *k2, const float *kl,
                                 const float *lse1, const float *lse2,

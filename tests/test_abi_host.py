@@ -174,6 +174,37 @@ def test_bwd_rejects_short_or_misaligned_workspace(lib):
     assert bwd(ws=0xC0004, wsb=need, **kw) == _lib.ERR_WORKSPACE
 
 
+def bwd_dq_ws(**kw):
+    a = dict(q1=A, k1=A2, q2=A3, k2=A4, kl=O1, lse1=O2, lse2=O3, dkl=None, B=1, H=2, NQ=64, NK=8192,
+             d=128, scale=0.125, causal=1, dtype=_lib.BF16, mask=3, dq1=0x80000, dq2=0xA0000,
+             ws=0xC0000, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = _lib.bwd_workspace_size(a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["causal"], a["dtype"],
+                                           a["mask"])
+    return _lib.bwd_dq_ws(a["q1"], a["k1"], a["q2"], a["k2"], a["kl"], a["lse1"], a["lse2"], a["dkl"],
+                          a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["scale"], a["causal"], a["dtype"],
+                          a["mask"], a["dq1"], a["dq2"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None, wsb=0), _lib.ERR_WORKSPACE), (dict(wsb=16), _lib.ERR_WORKSPACE),
+    (dict(ws=0xC0004), _lib.ERR_WORKSPACE),
+    (dict(mask=0), INV), (dict(mask=1, dq1=None), INV), (dict(mask=2, dq2=None), INV),
+    (dict(kl=None), INV), (dict(dq2=0xA0008), INV), (dict(d=96), UNS), (dict(NQ=8193), INV),
+])
+def test_bwd_dq_ws_rejects_bad_arguments(lib, kw, status):
+    assert bwd_dq_ws(**kw) == status
+
+
+def test_bwd_dq_ws_needs_workspace_only_where_the_query_grid_is_short(lib, no_gpu):
+    assert _lib.bwd_workspace_size(1, 2, 64, 8192, 128, 1, _lib.BF16, 3) > 0
+    assert bwd_dq_ws() == _lib.ERR_HIP                                   # partitioned: reaches the launch
+    assert _lib.bwd_workspace_size(2, 32, 8192, 8192, 128, 1, _lib.BF16, 3) == 0
+    assert bwd_dq_ws(B=2, H=32, NQ=8192, ws=None, wsb=0) == _lib.ERR_HIP  # unpartitioned: none needed
+    assert bwd_dq_ws(B=0, ws=None, wsb=0) == _lib.OK                    # nothing to do
+
+
 def test_unrequested_gradients_may_be_null(lib, no_gpu):
     assert bwd(mask=1, dq2=None, dk2=None) == _lib.ERR_HIP
     assert bwd(mask=2, dq1=None, dk1=None) == _lib.ERR_HIP

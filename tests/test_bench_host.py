@@ -88,3 +88,40 @@ def test_kernel_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     assert bench.kernel_hash("probe") == h0
     src.write_text("int f(int x) {\n  return x + 2;\n}\n")
     assert bench.kernel_hash("probe") != h0
+
+
+def test_cpu_baseline_times_what_the_step_computes(monkeypatch):
+    """The oracle sample runs the workload's own passes (the forward alone
+    for a forward-only workload), grows over whole heads once one head's rows
+    are not enough, and is credited per admissible pair as the GPU figure is
+    (16 d flops forward + backward, 4 d forward)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle
+    from attention_distillation_kl_amd.inputs import Workload
+
+    calls = []
+    real = oracle.head
+
+    def spy(*a, **kw):
+        calls.append((a[0].shape, kw["rows"], kw["grads"]))
+        return real(*a, **kw)
+
+    monkeypatch.setattr(oracle, "head", spy)
+    monkeypatch.setattr(bench.time, "perf_counter", iter(np.arange(0.0, 1e6, 0.01)).__next__)
+    g = torch.Generator().manual_seed(3)
+    for passes, causal, per_pair in (("fwd", False, 4), ("fwd+bwd", True, 16)):
+        w = Workload("t", 2, 3, 40, 56, 64, "f32", causal, "iid", 0.0, 1, passes)
+        q = [torch.randn(2, 3, 40, 64, generator=g) for _ in range(2)]
+        k = [torch.randn(2, 3, 56, 64, generator=g) for _ in range(2)]
+        calls.clear()
+        # Each timed run reads as 0.01 s: a 10 s target grows the sample to every head.
+        r = bench.cpu_baseline(w, q[0], k[0], q[1], k[1], 10.0)
+        assert all(c[2] == (passes == "fwd+bwd") for c in calls)
+        assert calls[-1][1] == (0, 40) and len({c[0] for c in calls}) == 1
+        nh = int(r["sample"].split("heads 0..")[1].split()[0]) + 1
+        assert nh == 6 and ("forward+backward" in r["sample"]) == (passes == "fwd+bwd")
+        keys = sum(min(56, i + 16 + 1) if causal else 56 for i in range(40))
+        assert abs(r["value"] * 0.01 * 1e12 - per_pair * 64 * keys * nh) < 1e-3 * per_pair * 64 * keys * nh

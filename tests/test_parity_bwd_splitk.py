@@ -70,3 +70,39 @@ def test_partitioned_query_gradients_are_deterministic_and_agree_with_one_partit
     for x, y in zip((a[0], a[2]), one):
         rel = ((x.double() - y.double()).norm() / y.double().norm()).item()
         assert rel < 4e-3, rel  # bf16 rounding of two fp32 summation orders
+
+
+# B, H, NQ, NK, d, causal, mask, partitioned
+HALF_CASES = [
+    (1, 4, 128, 8192, 128, True, 3, True),
+    (1, 2, 70, 3000, 64, True, 1, True),
+    (1, 32, 2048, 2048, 128, True, 3, False),
+]
+
+
+@pytest.mark.parametrize("case", HALF_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_halves_with_the_workspace_reproduce_streamkl_bwd(case):
+    """streamkl_bwd_dk then streamkl_bwd_dq_ws is streamkl_bwd, bit for bit,
+    whether or not the sizes call for key partitions."""
+    B, H, NQ, NK, d, causal, mask, partitioned = case
+    log(f"bwd halves with workspace {case}")
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=NQ + 7, device=DEV)
+    scale = d ** -0.5
+    g = upstream_grad(B, H, NQ, seed=11, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    full = ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
+    ws = ops.streamkl_bwd_workspace(q1, k1, causal, mask)
+    assert (ws is not None) == partitioned
+    if ws is None:  # the entry point with an empty workspace, which these sizes allow
+        ws = torch.empty(0, device=DEV, dtype=torch.uint8)
+    dk = ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
+    dq = ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask, workspace=ws)
+    torch.cuda.synchronize()
+    for got, want in zip((dq[0], dk[0], dq[1], dk[1]), full):
+        assert (got is None) == (want is None)
+        if want is not None:
+            assert torch.equal(got, want)
+    if partitioned:  # a workspace one granule short is refused before anything is enqueued
+        short = ws[: ws.numel() - 16]
+        with pytest.raises(_lib.StreamKLError, match="STREAMKL_ERR_WORKSPACE"):
+            ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask, workspace=short)
