@@ -88,8 +88,8 @@ struct BwdCfg {
   static constexpr int kNCst = 4;                         // per-row constant arrays
   static constexpr int kOffY2 = kTileChunks;              // Y2 within a stage
   static constexpr int kStage = 2 * kTileChunks;          // one stage: (Y1, Y2) tiles
-  static constexpr size_t kLdsBytes = size_t(2 * kStage + kXChunks + (PAIR ? kWaves * 128 : 0)) * 16 +
-                                      2 * kNCst * kBT * sizeof(float);  // the kernel's static LDS
+  static constexpr int kCstChunks = 2 * kNCst * kBT * int(sizeof(float)) / 16;  // both stages' constants
+  static constexpr size_t kLdsBytes = size_t(kCstChunks + 2 * kStage + kXChunks + (PAIR ? kWaves * 128 : 0)) * 16;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
   static_assert(kXChunks % kThreads == 0, "stationary tile must split evenly over the workgroup");
@@ -159,15 +159,16 @@ void bwd_kernel(BwdParams p) {
   constexpr bool kG1 = (MASK & 1) != 0;
   constexpr bool kG2 = (MASK & 2) != 0;
   constexpr int kMB = D / 32;  // 32-row blocks of d in the gradient accumulators
-  // LDS: the stages, the stationary tile and the row constants at fixed
+  // LDS: the row constants, the stages and the stationary tile at fixed
   // offsets of one dynamic array, the pairs' exchange slots in a static one.
   // From the constant offsets the compiler can tell that reading one stage
   // (or the constants, the stationary tile, the slots) need not wait for the
-  // copies in flight into the other stage.
+  // copies in flight into the other stage.  The constants come first: every
+  // read of them is then one lane offset plus an immediate below 64 KB.
   extern __shared__ u32x4 lds[];
-  u32x4 *ystage0 = lds, *ystage1 = lds + C::kStage;
-  u32x4 *xtile = lds + 2 * C::kStage;
-  float (*cstage)[C::kNCst * C::kBT] = reinterpret_cast<float (*)[C::kNCst * C::kBT]>(lds + 2 * C::kStage + C::kXChunks);
+  float (*cstage)[C::kNCst * C::kBT] = reinterpret_cast<float (*)[C::kNCst * C::kBT]>(lds);
+  u32x4 *ystage0 = lds + C::kCstChunks, *ystage1 = ystage0 + C::kStage;
+  u32x4 *xtile = ystage0 + 2 * C::kStage;
   __shared__ u32x4 xch[kPair ? C::kWaves * 128 : 1];          // pairs' exchange slots
 
   const int tid = threadIdx.x;
@@ -423,20 +424,48 @@ void bwd_kernel(BwdParams p) {
       // Without pairing, the MFMA bursts run at raised priority so that the
       // other wave on the SIMD keeps the vector unit busy meanwhile (paired
       // waves gain nothing from it).
-      if (!kPair) __builtin_amdgcn_s_setprio(2);
+      if constexpr (kPair) {
+        // The fragments are read kAhead chunks ahead of their products, into
+        // a ring of registers, so the products of one chunk run while the
+        // reads of the next ones are in flight.
+        constexpr int kAhead = 3;
+        u32x4 f1[kAhead + 1], f2[kAhead + 1];
+        auto frag = [&](int cc) {
+          const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
+          f1[cc % (kAhead + 1)] = ybase[pos];
+          f2[cc % (kAhead + 1)] = ybase[C::kOffY2 + pos];
+        };
 #pragma unroll
-      for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-        const int fc = frag_chunk<BF16, D>(h, cc);
-        const int pos = arow * G::kChunks + swz<G::kChunks>(arow, fc);
-        if constexpr (C::kX1Lds) {
-          const u32x4 x1 = xtile[xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
-          mfma_chunk<BF16>(ybase[pos], x1, s1);
-        } else {
-          mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+        for (int cc = 0; cc < kAhead; ++cc) frag(cc);
+#pragma unroll
+        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+          if (cc + kAhead < G::kLaneChunks) frag(cc + kAhead);
+          mfma_chunk<BF16>(f1[cc % (kAhead + 1)], xf1[cc], s1);
+          mfma_chunk<BF16>(f2[cc % (kAhead + 1)], xf2[cc], s2);
         }
-        mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // the first chunks' reads
+#pragma unroll
+        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+          if (cc + kAhead < G::kLaneChunks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);          // chunk cc's products
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+          const int fc = frag_chunk<BF16, D>(h, cc);
+          const int pos = arow * G::kChunks + swz<G::kChunks>(arow, fc);
+          if constexpr (C::kX1Lds) {
+            const u32x4 x1 = xtile[xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
+            mfma_chunk<BF16>(ybase[pos], x1, s1);
+          } else {
+            mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+          }
+          mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
+        }
+        __builtin_amdgcn_s_setprio(0);
       }
-      if (!kPair) __builtin_amdgcn_s_setprio(0);
     };
 
     // 2. regenerate P and form e1, e2 (fp32).
