@@ -421,13 +421,12 @@ void bwd_kernel(BwdParams p) {
       }
       const int arow = sb * 32 + col;
       const int xrow = wrow * 32 + col;  // the lane's stationary row in the LDS tile
-      // Without pairing, the MFMA bursts run at raised priority so that the
-      // other wave on the SIMD keeps the vector unit busy meanwhile (paired
-      // waves gain nothing from it).
       if constexpr (kPair) {
         // The fragments are read kAhead chunks ahead of their products, into
-        // a ring of registers, so the products of one chunk run while the
-        // reads of the next ones are in flight.
+        // a ring of registers.  While tile copies are in flight the compiler
+        // waits for LDS reads only all at once (lgkmcnt(0)), so each wait
+        // drains the ring: with three chunks in flight a product pair waits
+        // once every four chunks instead of once per chunk.
         constexpr int kAhead = 3;
         u32x4 f1[kAhead + 1], f2[kAhead + 1];
         auto frag = [&](int cc) {
@@ -451,6 +450,9 @@ void bwd_kernel(BwdParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
+        // Without pairing, the MFMA bursts run at raised priority so that the
+        // other wave on the SIMD keeps the vector unit busy meanwhile (paired
+        // waves gain nothing from it).
         __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int cc = 0; cc < G::kLaneChunks; ++cc) {
