@@ -61,7 +61,7 @@ enum { ROLE_DQ = 0, ROLE_DK = 1 };
 // stationary rows.  Per streamed tile each recomputes the scores of one of the
 // two 32-row blocks and forms e1, e2 there; they swap one of the two through
 // LDS, and then wave 0 accumulates the teacher's gradient and wave 1 the
-// student's over both blocks.  A wave then holds one d x 32 accumulator
+// student's over both blocks, each starting with the block it scored.  A wave then holds one d x 32 accumulator
 // instead of two and both stationary fragments fit in registers at two waves
 // per SIMD.
 // Otherwise (one gradient, or fp32) every wave owns its own 32 stationary rows
@@ -366,8 +366,9 @@ void bwd_kernel(BwdParams p) {
   // One streamed tile.  `stage_c` is the LDS buffer as a compile-time
   // constant, so every LDS address below is a loop-invariant lane offset plus
   // an immediate; the loop is unrolled by two to alternate the buffers.
-  auto tile_step = [&](int it, auto stage_c) {
+  auto tile_step = [&](int it, auto stage_c, auto half_c) {
     constexpr int stage = decltype(stage_c)::value;
+    constexpr int hc = decltype(half_c)::value;  // the wave's half of a pair, as a constant
     const int tile = tile0 + it;
     // Buffer stage^1 was last read in iteration it-1, which ended in a barrier.
     if (it + 1 < ntiles) {
@@ -427,7 +428,7 @@ void bwd_kernel(BwdParams p) {
         // waits for LDS reads only all at once (lgkmcnt(0)), so each wait
         // drains the ring: with three chunks in flight a product pair waits
         // once every four chunks instead of once per chunk.
-        constexpr int kAhead = 3;
+        constexpr int kAhead = CAUSAL ? 3 : 2;  // non-causal: the deeper ring spills
         u32x4 f1[kAhead + 1], f2[kAhead + 1];
         auto frag = [&](int cc) {
           const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
@@ -571,16 +572,16 @@ void bwd_kernel(BwdParams p) {
     if constexpr (kPair) {
       f32x16 s1, s2;
       EBlock E;
-      scores(half, s1, s2, straddles(half));
-      form(half, s1, s2, E);
+      scores(hc, s1, s2, straddles(hc));
+      form(hc, s1, s2, E);
       // Keep the operand of the gradient this wave accumulates; hand the
       // other to the partner, which scored the other block.
-      u32x4 mine[2], theirs[2], b0[2], b1[2];
+      u32x4 mine[2], theirs[2];
       u32x4 *slot = xch + wave * 128 + lane;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        mine[ks] = half ? E.pk2[ks] : E.pk1[ks];
-        slot[64 * ks] = half ? E.pk1[ks] : E.pk2[ks];
+        mine[ks] = hc ? E.pk2[ks] : E.pk1[ks];
+        slot[64 * ks] = hc ? E.pk1[ks] : E.pk2[ks];
       }
       // Barrier that waits for this wave's LDS stores only (lgkmcnt), not
       // for the tile copies in flight; the empty asm statements keep the
@@ -591,17 +592,21 @@ void bwd_kernel(BwdParams p) {
       asm volatile("" ::: "memory");
       const u32x4 *peer = xch + (wave ^ 1) * 128 + lane;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        theirs[ks] = peer[64 * ks];
-        b0[ks] = half ? theirs[ks] : mine[ks];
-        b1[ks] = half ? mine[ks] : theirs[ks];
-      }
-      const char *yb = reinterpret_cast<const char *>(ybase + half * C::kOffY2);
-      grad_bf16(0, yb, b0, acc1);
-      grad_bf16(1, yb, b1, acc1);
+      for (int ks = 0; ks < 2; ++ks) theirs[ks] = peer[64 * ks];
+      // Each wave adds its own block first, so its first products need no
+      // data from the partner.  The student's gradient thus takes the blocks
+      // in the order 1, 0, as the unpaired kernel does for it.
+      const char *yb = reinterpret_cast<const char *>(ybase + hc * C::kOffY2);
+      grad_bf16(hc, yb, mine, acc1);
+      grad_bf16(1 - hc, yb, theirs, acc1);
     } else {
+      // The key-gradient role with the student's gradient alone takes the
+      // blocks in the order the paired kernel's student wave does (its own
+      // block, 1, first), so both give the same bits.
+      constexpr bool kRev = BF16 && ROLE == ROLE_DK && MASK == 2;
 #pragma unroll
-      for (int sb = 0; sb < C::kSub; ++sb) {
+      for (int i = 0; i < C::kSub; ++i) {
+        const int sb = kRev ? C::kSub - 1 - i : i;
         f32x16 s1, s2;
         EBlock E;
         scores(sb, s1, s2, straddles(sb));
@@ -615,9 +620,20 @@ void bwd_kernel(BwdParams p) {
     __syncthreads();  // also waits for the copies into stage^1
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
-    tile_step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{});
+  auto run = [&](auto half_c) {
+    for (int it = 0; it < ntiles; it += 2) {
+      tile_step(it, std::integral_constant<int, 0>{}, half_c);
+      if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{}, half_c);
+    }
+  };
+  // A pair's two waves run their own copy of the loop, in which the half is a
+  // constant: which operand a wave keeps, hands over and adds first is then
+  // fixed.  (half is wave-uniform.)
+  if constexpr (kPair) {
+    if (half) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
   }
 
   // ---------------------------------------------------------------- write-out
