@@ -268,6 +268,12 @@ void bwd_kernel(BwdParams p) {
   // Full tiles take 32-bit offsets from the head's base (where a head's rows
   // span fewer than 2^32 bytes): one per copy, a constant apart.  The last
   // tile, and heads of 4 GiB or more, use 64-bit offsets and clamp each row.
+  // The key-gradient role issues its 32-bit-offset copies unseen by the
+  // compiler (dma16_unseen): its transposing reads carry no alias
+  // information, so a visible copy would make the first of them wait for the
+  // copy in flight, and every LDS wait meanwhile would be lgkmcnt(0).  The
+  // query-gradient role measured no faster that way and keeps the builtin.
+  constexpr bool kUnseen = ROLE == ROLE_DK;
   const bool off32 = size_t(nt) * G::kRowBytes <= size_t(0xFFFFFFFFu);
   auto issue = [&](int tile, int stage) {
     u32x4 *wbase = (stage ? ystage1 : ystage0) + wave * 64;
@@ -278,8 +284,13 @@ void bwd_kernel(BwdParams p) {
         const int row = pos / G::kChunks;
         const int ch = swz<G::kChunks>(row, pos % G::kChunks);
         const uint32_t o = uint32_t(tile * C::kBT + row) * G::kRowBytes + uint32_t(ch * 16);
-        dma16(Y1 + o, wbase + i * C::kThreads);
-        dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
+        if constexpr (kUnseen) {
+          dma16_unseen(Y1, o, wbase + i * C::kThreads);
+          dma16_unseen(Y2, o, wbase + i * C::kThreads + C::kOffY2);
+        } else {
+          dma16(Y1 + o, wbase + i * C::kThreads);
+          dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
+        }
       }
     } else {
 #pragma unroll
@@ -354,6 +365,7 @@ void bwd_kernel(BwdParams p) {
     issue(tile0, 0);
     cstore(0);
   }
+  if constexpr (kUnseen) vmcnt0_wait();  // copies the compiler's own waits do not cover
   __syncthreads();
 
   // e1/e2 of one 32-row block in the form the gradient product consumes:
@@ -423,12 +435,10 @@ void bwd_kernel(BwdParams p) {
       const int arow = sb * 32 + col;
       const int xrow = wrow * 32 + col;  // the lane's stationary row in the LDS tile
       if constexpr (kPair) {
-        // The fragments are read kAhead chunks ahead of their products, into
-        // a ring of registers.  While tile copies are in flight the compiler
-        // waits for LDS reads only all at once (lgkmcnt(0)), so each wait
-        // drains the ring: with three chunks in flight a product pair waits
-        // once every four chunks instead of once per chunk.
-        constexpr int kAhead = CAUSAL ? 3 : 2;  // non-causal: the deeper ring spills
+        // The fragments are read one chunk ahead of their products, into a
+        // second pair of registers, so the products of one chunk run while
+        // the next chunk's reads are in flight.
+        constexpr int kAhead = 1;
         u32x4 f1[kAhead + 1], f2[kAhead + 1];
         auto frag = [&](int cc) {
           const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
@@ -617,7 +627,8 @@ void bwd_kernel(BwdParams p) {
     }
 
     if (it + 1 < ntiles) cstore(stage ^ 1);
-    __syncthreads();  // also waits for the copies into stage^1
+    if constexpr (kUnseen) vmcnt0_wait();  // the copies into stage^1
+    __syncthreads();  // also waits for the copies the compiler sees
   };
 
   auto run = [&](auto half_c) {

@@ -132,6 +132,29 @@ __device__ __forceinline__ void dma16(const void *gsrc, u32x4 *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
 }
 
+// The same copy, from a wave-uniform 64-bit base plus a 32-bit lane offset,
+// issued as inline assembly so that the compiler does not see it.  The
+// compiler then neither waits for it before LDS reads it cannot tell apart
+// from its target (the transposing reads) nor treats LDS reads as unordered
+// while it is in flight.  The caller owns its completion: s_waitcnt vmcnt(0)
+// (vmcnt0_wait below) before the barrier that publishes the tile.  The copy
+// writes no register; m0 is set and declared clobbered in the same statement
+// (one wait state between the m0 write and the copy).
+__device__ __forceinline__ void dma16_unseen(const void *sbase, uint32_t voff, u32x4 *lds_wave_base) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_char *)(reinterpret_cast<char *>(lds_wave_base))));
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory", "m0");
+}
+
+// Wait for every vector-memory load of the wave, copies included.
+__device__ __forceinline__ void vmcnt0_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // Pack two fp32 values to bf16 (round to nearest even) in one dword.
