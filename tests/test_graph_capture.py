@@ -1,0 +1,63 @@
+"""The library's calls inside a captured HIP graph.
+
+The library allocates nothing, keeps no state and issues no memset or
+synchronisation, so a forward and a backward can be captured into one graph
+(outputs and workspaces come from torch's graph pool) and replayed.  Each
+replay must give the eager results bit for bit: the kernels are
+deterministic and the library's choices (partitions, workspace) depend on
+the sizes only.  Eager work and synchronisations run between the replays.
+"""
+import pytest
+import torch
+
+from attention_distillation_kl_amd import make_inputs, ops
+from attention_distillation_kl_amd.inputs import upstream_grad
+from parity_util import log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+# B, H, NQ, NK, d, causal: a shape that fills the GPU with the plain kernels,
+# and a short query block that takes the split-K forward and the
+# key-partitioned backward (both with workspace).
+CASES = [(1, 32, 4096, 4096, 128, False), (1, 4, 64, 8192, 128, True)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_forward_and_backward_replay_from_a_captured_graph(case):
+    B, H, NQ, NK, d, causal = case
+    log(f"graph capture {case}")
+    from attention_distillation_kl_amd import _lib
+    plain = _lib.fwd_splits(B, H, NQ, NK, d, int(causal), _lib.BF16) == 1
+    assert plain == (_lib.bwd_workspace_size(B, H, NQ, NK, d, int(causal), _lib.BF16, 3) == 0)
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=NQ + 3, device=DEV)
+    g = upstream_grad(B, H, NQ, seed=9, device=DEV)
+    scale = d ** -0.5
+
+    def step():
+        kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
+        return (kl, l1, l2) + tuple(ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal))
+
+    want = step()
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream's side, as torch recommends
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = step()
+    for rep in range(3):
+        other = step()  # eager work between replays, on the same allocator
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, y, z in zip(("kl", "lse1", "lse2", "dq1", "dk1", "dq2", "dk2"), got, want, other):
+            assert torch.equal(x, y), (rep, name)
+            assert torch.equal(z, y), (rep, name, "eager")
