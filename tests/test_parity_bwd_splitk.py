@@ -76,6 +76,9 @@ def test_partitioned_query_gradients_are_deterministic_and_agree_with_one_partit
 HALF_CASES = [
     (1, 4, 128, 8192, 128, True, 3, True),
     (1, 2, 70, 3000, 64, True, 1, True),
+    (1, 3, 1, 8192, 64, False, 3, True),      # decoding row
+    (1, 2, 70, 3000, 128, False, 2, True),
+    (2, 2, 33, 5000, 64, True, 1, True),
     (1, 32, 2048, 2048, 128, True, 3, False),
 ]
 
