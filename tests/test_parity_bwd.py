@@ -79,13 +79,17 @@ def test_bwd_c2_full():
     compare_all_heads(q1, k1, q2, k2, w.scale, w.causal, tag="c2")
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (64, True), (128, False)])
 @pytest.mark.parametrize("mask", [1, 2])
-def test_bwd_single_configuration_masks(mask):
+def test_bwd_single_configuration_masks(mask, d, causal):
     """grad_mask = 1 (Configuration 2) / 2 (Configuration 1) produce exactly the
-    corresponding tensors of the full backward and leave the others alone."""
-    q1, k1, q2, k2 = make_inputs(1, 2, 300, 300, 128, torch.bfloat16, "student", 0.3, seed=12, device=DEV)
-    _, full = fwd_bwd(q1, k1, q2, k2, 0.09, True)
-    _, part = fwd_bwd(q1, k1, q2, k2, 0.09, True, mask=mask)
+    corresponding tensors of the full backward and leave the others alone.
+    (In bf16 the full backward's key gradients come from the paired kernel,
+    the single ones from the unpaired kernel: both add the streamed blocks in
+    the same order.)"""
+    q1, k1, q2, k2 = make_inputs(1, 2, 300, 300, d, torch.bfloat16, "student", 0.3, seed=12, device=DEV)
+    _, full = fwd_bwd(q1, k1, q2, k2, 0.09, causal)
+    _, part = fwd_bwd(q1, k1, q2, k2, 0.09, causal, mask=mask)
     keep = ("dq1", "dk1") if mask == 1 else ("dq2", "dk2")
     for n in NAMES:
         if n in keep:
