@@ -51,6 +51,24 @@ class Workload:
         """16 * N_Q * N_K * d per head (fwd 4 + bwd 12), halved when causal."""
         return 4.0 * self.fwd_flops()
 
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def fwd_bytes(self) -> float:
+        """Algorithmic HBM bytes of one forward: Q1, Q2, K1, K2 read once,
+        KL, LSE1, LSE2 written (12 B per query row)."""
+        bh = self.B * self.H
+        return float(bh * (2 * (self.NQ + self.NK) * self.d * self.elem_bytes() + 12 * self.NQ))
+
+    def bwd_bytes(self, kernel: str) -> float:
+        """Algorithmic HBM bytes of one backward kernel: the four inputs and
+        16 B per query row (KL, LSE1, LSE2, upstream gradient) read, its two
+        gradients written ('bwd_dk': dK1, dK2; 'bwd_dq': dQ1, dQ2)."""
+        bh = self.B * self.H
+        rows = self.NK if kernel == "bwd_dk" else self.NQ
+        return float(bh * (2 * (self.NQ + self.NK) * self.d * self.elem_bytes() + 16 * self.NQ
+                           + 2 * rows * self.d * self.elem_bytes()))
+
     def as_dict(self):
         return asdict(self)
 
@@ -62,6 +80,8 @@ WORKLOADS = {
     "c4": Workload("c4", 1, 32, 2048, 65536, 128, "bf16", False, "iid", 0.0, 1004, "fwd"),
     "c5": Workload("c5", 1, 32, 65536, 65536, 128, "bf16", True, "student", 0.2, 1005, "fwd+bwd"),
     "h32k": Workload("h32k", 1, 32, 32768, 32768, 128, "bf16", True, "student", 0.2, 1032, "fwd+bwd"),
+    # one decoding row per head over 64K keys (the split-K forward's case)
+    "decode": Workload("decode", 1, 32, 1, 65536, 128, "bf16", False, "iid", 0.0, 1006, "fwd"),
 }
 
 

@@ -21,6 +21,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 CSRC = os.path.join(ROOT, "attention_distillation_kl_amd", "csrc")
 # Sources of each kernel's translation unit: the traffic counters recorded in
@@ -258,6 +259,18 @@ def sweep(args):
         n *= 2
 
 
+def roofline_bound(w, kernel, peak_tflops):
+    """(bound, algorithmic work per launch, peak, unit) of one timed kernel:
+    HBM when its flops per algorithmic byte fall below the machine balance
+    (peak flops / HBM bandwidth), MFMA otherwise."""
+    fwd_fl = w.fwd_flops()
+    flops = fwd_fl if kernel == "fwd" else 2 * fwd_fl
+    nbytes = w.fwd_bytes() if kernel == "fwd" else w.bwd_bytes(kernel)
+    if flops / nbytes < peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        return "hbm", nbytes, PEAK_HBM_GBS, "GB/s"
+    return "mfma", flops, peak_tflops, "TFLOP/s"
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -339,15 +352,19 @@ def main():
     value = total_fl / (step_ms * 1e-3) / 1e12
     fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
 
-    # Dominant kernel: the one with the largest average duration.  Its MFMA
-    # work per launch: forward 4 N_Q N_K d per head; each backward kernel
-    # recomputes both score blocks (4) and forms two gradients (4): 8 N_Q N_K d.
-    per_launch = {"fwd": fwd_fl, "bwd_dk": 2 * fwd_fl, "bwd_dq": 2 * fwd_fl}
+    # Dominant kernel: the one with the largest average duration.  Its
+    # algorithmic work per launch: forward 4 N_Q N_K d flops per head; each
+    # backward kernel recomputes both score blocks (4) and forms two gradients
+    # (4): 8 N_Q N_K d.  Workloads below the machine balance (decoding rows)
+    # are priced in algorithmic HBM bytes against the HBM bandwidth instead.
     dom = max(kern, key=kern.get)
-    ach = per_launch[dom] / (kern[dom] * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, dom),
-            "flops_per_launch": per_launch[dom], "avg_launch_ms": round(kern[dom], 4)}
+    bound, work, rpeak, runit = roofline_bound(w, dom, peak)
+    scale_unit = 1e12 if runit == "TFLOP/s" else 1e9
+    ach = work / (kern[dom] * 1e-3) / scale_unit
+    roof = {"bound": bound, "kernel": dom, "achieved": round(ach, 2), "peak": rpeak, "unit": runit,
+            "frac": round(ach / rpeak, 4), "traffic": recorded_traffic(w.name, dom),
+            ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work,
+            "avg_launch_ms": round(kern[dom], 4)}
 
     # The graphics clock, sampled while untimed steps keep the GPU busy (the
     # clock drops within milliseconds once the GPU idles).

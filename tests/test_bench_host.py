@@ -125,3 +125,20 @@ def test_cpu_baseline_times_what_the_step_computes(monkeypatch):
         assert nh == 6 and ("forward+backward" in r["sample"]) == (passes == "fwd+bwd")
         keys = sum(min(56, i + 16 + 1) if causal else 56 for i in range(40))
         assert abs(r["value"] * 0.01 * 1e12 - per_pair * 64 * keys * nh) < 1e-3 * per_pair * 64 * keys * nh
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """Kernels whose flops per algorithmic byte fall below the machine balance
+    (decoding rows) are priced against HBM bandwidth, the rest against MFMA;
+    the byte counts are the inputs read once, the row vectors and the outputs."""
+    sys.path.insert(0, ROOT)
+    import bench
+    h, dec = WORKLOADS["h32k"], WORKLOADS["decode"]
+    for k in ("fwd", "bwd_dk", "bwd_dq"):
+        assert bench.roofline_bound(h, k, 2500.0)[0] == "mfma"
+    bound, nbytes, peak, unit = bench.roofline_bound(dec, "fwd", 2500.0)
+    assert (bound, peak, unit) == ("hbm", 8000.0, "GB/s")
+    assert nbytes == 32 * (2 * (1 + 65536) * 128 * 2 + 12 * 1)
+    n = 32768
+    assert h.bwd_bytes("bwd_dk") == 32 * (2 * 2 * n * 128 * 2 + 16 * n + 2 * n * 128 * 2)
+    assert h.fwd_bytes() == 32 * (2 * 2 * n * 128 * 2 + 12 * n)
