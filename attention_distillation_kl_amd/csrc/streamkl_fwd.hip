@@ -42,12 +42,13 @@
 namespace streamkl {
 namespace {
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool RM = false>
 struct FwdCfg {
   using G = RowGeom<BF16, D>;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kNQB = (BF16 || D == 64) ? 2 : 1;  // 32-query blocks per wave
+  // 32-query blocks per wave; the row-major form (decoding rows) takes one.
+  static constexpr int kNQB = RM ? 1 : (BF16 || D == 64) ? 2 : 1;
   static constexpr int kWQ = 32 * kNQB;                   // queries per wave
   static constexpr int kBQ = kWQ * kWaves;                // queries per workgroup
   static constexpr int kBK = BF16 ? 64 : 32;              // keys per LDS tile
@@ -74,10 +75,14 @@ struct FwdParams {
 // row r (r = bh * N_Q + i) of `rows` rows lives at part[(k * nsplit + s) * rows + r].
 enum { ST_M1 = 0, ST_M2, ST_L1, ST_L2, ST_ACC, ST_N };
 
-template <bool BF16, int D, bool CAUSAL, bool SPLIT>
+// RM: key tiles stored row-major with the backward's XOR swizzle instead of
+// chunk-major.  Each copy instruction then reads whole key rows (coalesced);
+// the fragment reads need one address per chunk.  Used for decoding rows,
+// which are bound by the copies, not by the products.
+template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool RM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
-  using C = FwdCfg<BF16, D>;
+  using C = FwdCfg<BF16, D, RM>;
   using G = typename C::G;
   constexpr int NQB = C::kNQB;
   extern __shared__ u32x4 lds[];  // [stage][tensor][kTileChunks]
@@ -166,6 +171,20 @@ void fwd_kernel(FwdParams p) {
   const int crow = tid % C::kBK;                // the tile row this thread copies
   const int cch = tid / C::kBK;                 // its first chunk; then every kThreads/kBK
   auto issue = [&](int kt, int stage) {
+    if constexpr (RM) {
+      // Lane L of wave w fills position i*threads + 64w + L of the row-major
+      // tile; the global side reads the (row, logical chunk) stored there.
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int pos = i * C::kThreads + tid;
+        const int row = pos / G::kChunks;
+        const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+        const size_t o = size_t(min(kt * C::kBK + row, p.nk - 1)) * G::kRowBytes + ch * 16;
+        dma16(kb1 + o, lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64);
+        dma16(kb2 + o, lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64);
+      }
+      return;
+    }
     const int key = min(kt * C::kBK + crow, p.nk - 1);
     const size_t o = size_t(key) * G::kRowBytes + cch * 16;
 #pragma unroll
@@ -241,7 +260,8 @@ void fwd_kernel(FwdParams p) {
     const int row = sb * 32 + col;
 #pragma unroll
     for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-      const int pos = frag_chunk<BF16, D>(h, cc) * C::kBK + row;
+      const int pos = RM ? row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc))
+                         : frag_chunk<BF16, D>(h, cc) * C::kBK + row;
       mfma_chunk<BF16>(t1[pos], qf1[j][cc], s1);
       mfma_chunk<BF16>(t2[pos], qf2[j][cc], s2);
     }
@@ -296,7 +316,8 @@ void fwd_kernel(FwdParams p) {
       __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
-        const int pos = frag_chunk<BF16, D>(h, cc) * C::kBK + row;
+        const int pos = RM ? row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc))
+                           : frag_chunk<BF16, D>(h, cc) * C::kBK + row;
         const u32x4 a1 = b1[pos], a2 = b2[pos];
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
@@ -423,9 +444,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
   lse2[r] = l2;
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool RM = false>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-  using C = FwdCfg<BF16, D>;
+  using C = FwdCfg<BF16, D, RM>;
   FwdParams p;
   p.q1 = static_cast<const char *>(a.q1);
   p.k1 = static_cast<const char *>(a.k1);
@@ -449,8 +470,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   void *args[] = {&p};
-  const void *fn = split ? reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, true>)
-                         : reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, false>);
+  const void *fn = split ? reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, true, RM>)
+                         : reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, false, RM>);
   hipError_t e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
   if (e != hipSuccess || !split) return e;
   const size_t mblocks = (p.rows + 255) / 256;
@@ -487,6 +508,12 @@ int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal) {
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
+  // Decoding rows (key partitions whose query rows fit one wave): row-major
+  // key tiles, whose copies read whole rows.
+  if (a.bf16 && a.splits > 1 && a.nq <= FwdCfg<true, 128>::kWQ) {
+    if (a.d == 64) return a.causal ? launch<true, 64, true, true>(a, stream) : launch<true, 64, false, true>(a, stream);
+    return a.causal ? launch<true, 128, true, true>(a, stream) : launch<true, 128, false, true>(a, stream);
+  }
   if (a.bf16) {
     if (a.d == 64) return a.causal ? launch<true, 64, true>(a, stream) : launch<true, 64, false>(a, stream);
     return a.causal ? launch<true, 128, true>(a, stream) : launch<true, 128, false>(a, stream);

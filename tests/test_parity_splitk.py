@@ -42,6 +42,7 @@ CASES = [
     (1, 1, 37, 130, 128, "f32", False, 7),
     (1, 2, 17, 63, 64, "bf16", True, 4),       # one key tile, four partitions
     (1, 3, 1, 4096, 128, "bf16", False, 16),   # decoding: one query row
+    (1, 2, 64, 3000, 128, "bf16", True, 6),    # rows for two waves, ragged key tail
     (1, 1, 257, 2048, 64, "bf16", True, 9),
 ]
 
