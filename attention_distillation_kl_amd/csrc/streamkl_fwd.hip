@@ -50,9 +50,14 @@ struct FwdCfg {
   // 32-query blocks per wave; the row-major form (decoding rows) takes one.
   static constexpr int kNQB = RM ? 1 : (BF16 || D == 64) ? 2 : 1;
   static constexpr int kWQ = 32 * kNQB;                   // queries per wave
-  static constexpr int kBQ = kWQ * kWaves;                // queries per workgroup
   static constexpr int kBK = BF16 ? 64 : 32;              // keys per LDS tile
   static constexpr int kSub = kBK / 32;                   // 32-key blocks per tile
+  // Waves sharing one query block, each scoring its own 32-key blocks of
+  // every tile (the row-major form: decoding rows leave most waves of a
+  // workgroup without rows of their own).
+  static constexpr int kKSplit = RM ? kSub : 1;
+  static constexpr int kBQ = kWQ * kWaves / kKSplit;      // queries per workgroup
+  static_assert(kWaves % kKSplit == 0 && kSub % kKSplit == 0, "waves must pair evenly");
   static constexpr int kTileChunks = kBK * G::kChunks;    // 16-B chunks per tensor tile
   static constexpr int kLoads = kTileChunks / kThreads;   // copies per thread per tensor
   static constexpr size_t kLdsBytes = size_t(2) * 2 * kTileChunks * 16;  // 2 stages x K1,K2
@@ -77,8 +82,10 @@ enum { ST_M1 = 0, ST_M2, ST_L1, ST_L2, ST_ACC, ST_N };
 
 // RM: key tiles stored row-major with the backward's XOR swizzle instead of
 // chunk-major.  Each copy instruction then reads whole key rows (coalesced);
-// the fragment reads need one address per chunk.  Used for decoding rows,
-// which are bound by the copies, not by the products.
+// the fragment reads need one address per chunk.  Used for decoding rows.
+// There two waves share each 32-query block, each scoring one of a tile's
+// two 32-key blocks, so twice as many waves fold scores; their states are
+// merged at the end.
 template <bool BF16, int D, bool CAUSAL, bool SPLIT, bool RM = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
@@ -103,7 +110,10 @@ void fwd_kernel(FwdParams p) {
   const int qbr = rem - split * p.nqb;
   const int qb = CAUSAL ? p.nqb - 1 - qbr : qbr;
   const int q0 = qb * C::kBQ;
-  const int wq0 = q0 + wave * C::kWQ;
+  // The wave's query block and, with kKSplit > 1, which 32-key blocks of a
+  // tile it scores (those with sb % kKSplit == ksub).
+  const int ksub = wave % C::kKSplit;
+  const int wq0 = q0 + (wave / C::kKSplit) * C::kWQ;
   const bool wave_active = wq0 < p.nq;
 
   const size_t qoff = size_t(bh) * p.nq * G::kRowBytes;
@@ -301,6 +311,7 @@ void fwd_kernel(FwdParams p) {
 
 #pragma unroll
     for (int sb = 0; sb < C::kSub; ++sb) {
+      if (C::kKSplit > 1 && sb % C::kKSplit != ksub) continue;  // another wave's keys
       const int kb = kt * C::kBK + sb * 32;
       if (!wave_active || kb > w_hi) continue;  // past every row's frontier
 
@@ -378,14 +389,42 @@ void fwd_kernel(FwdParams p) {
     const float om1 = __shfl_xor(m1[j], 32), om2 = __shfl_xor(m2[j], 32);
     const float ol1 = __shfl_xor(l1[j], 32), ol2 = __shfl_xor(l2[j], 32);
     const float oacc = __shfl_xor(acc[j], 32);
-    const float M1 = vmax(m1[j], om1), M2 = vmax(m2[j], om2);
+    float M1 = vmax(m1[j], om1), M2 = vmax(m2[j], om2);
     const float fa1 = (m1[j] == -INFINITY) ? 0.f : fast_exp2((m1[j] - M1) * c);
     const float fb1 = (om1 == -INFINITY) ? 0.f : fast_exp2((om1 - M1) * c);
     const float fa2 = (m2[j] == -INFINITY) ? 0.f : fast_exp2((m2[j] - M2) * c);
     const float fb2 = (om2 == -INFINITY) ? 0.f : fast_exp2((om2 - M2) * c);
-    const float L1 = l1[j] * fa1 + ol1 * fb1;
-    const float L2 = l2[j] * fa2 + ol2 * fb2;
-    const float A = acc[j] * fa1 + oacc * fb1;
+    float L1 = l1[j] * fa1 + ol1 * fb1;
+    float L2 = l2[j] * fa2 + ol2 * fb2;
+    float A = acc[j] * fa1 + oacc * fb1;
+    if constexpr (C::kKSplit > 1) {
+      // Merge the waves that scored disjoint key blocks of the same rows, the
+      // same way, through LDS: the tile buffers are free, since the loop
+      // ended in a barrier after its last reads and no copy is in flight.
+      static_assert(C::kKSplit == 2 && NQB == 1, "one partner wave, one query block");
+      float *x = reinterpret_cast<float *>(lds) + (wave / 2) * (ST_N * 32) + col;
+      __syncthreads();
+      if (ksub == 1 && h == 0) {
+        x[ST_M1 * 32] = M1;
+        x[ST_M2 * 32] = M2;
+        x[ST_L1 * 32] = L1;
+        x[ST_L2 * 32] = L2;
+        x[ST_ACC * 32] = A;
+      }
+      __syncthreads();
+      if (ksub == 1) continue;  // the even wave of the pair writes the rows
+      const float pm1 = x[ST_M1 * 32], pm2 = x[ST_M2 * 32];
+      const float N1 = vmax(M1, pm1), N2 = vmax(M2, pm2);
+      const float ga1 = (M1 == -INFINITY) ? 0.f : fast_exp2((M1 - N1) * c);
+      const float gb1 = (pm1 == -INFINITY) ? 0.f : fast_exp2((pm1 - N1) * c);
+      const float ga2 = (M2 == -INFINITY) ? 0.f : fast_exp2((M2 - N2) * c);
+      const float gb2 = (pm2 == -INFINITY) ? 0.f : fast_exp2((pm2 - N2) * c);
+      L1 = L1 * ga1 + x[ST_L1 * 32] * gb1;
+      L2 = L2 * ga2 + x[ST_L2 * 32] * gb2;
+      A = A * ga1 + x[ST_ACC * 32] * gb1;
+      M1 = N1;
+      M2 = N2;
+    }
     const int qrow = wq0 + 32 * j + col;
     if (SPLIT) {
       // The partition's state, merged with the others by merge_kernel.
