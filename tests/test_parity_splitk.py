@@ -44,6 +44,8 @@ CASES = [
     (1, 3, 1, 4096, 128, "bf16", False, 16),   # decoding: one query row
     (1, 2, 64, 3000, 128, "bf16", True, 6),    # rows for two waves, ragged key tail
     (1, 1, 257, 2048, 64, "bf16", True, 9),
+    (1, 1, 5, 20, 128, "bf16", False, 2),      # under 32 keys: one wave of each pair scores none
+    (1, 2, 20, 20, 128, "bf16", True, 3),      # the same, causal, with empty partitions
 ]
 
 
