@@ -86,6 +86,7 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="context-length sweep instead of the headline: N = 4K..--sweep-max, "
                          "forward and each backward configuration, causal and not; one JSON line per N")
+    ap.add_argument("--sweep-min", type=int, default=4096)
     ap.add_argument("--sweep-max", type=int, default=524288)
     ap.add_argument("--sweep-heads", type=int, default=32)
     return ap.parse_args()
@@ -198,7 +199,8 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s):
 
 def sweep(args):
     """Latency and memory against context length, on the axes of the page's
-    results ("Risultati Sperimentali": 4K to 512K tokens; forward latency,
+    results ("Risultati Sperimentali": 4K to 512K tokens, doubling from
+    --sweep-min; forward latency,
     causal and not; backward latency of Configuration 1 and Configuration 2;
     memory footprint).  B = 1, H = --sweep-heads, d = 128, bf16, student =
     teacher + 0.2 N(0,1).  For each N and mask the times are HIP events around
@@ -211,7 +213,7 @@ def sweep(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     H, d = args.sweep_heads, 128
-    n = 4096
+    n = getattr(args, "sweep_min", 4096)
     while n <= args.sweep_max:
         q1, k1, q2, k2 = make_inputs(1, H, n, n, d, torch.bfloat16, "student", 0.2,
                                      seed=2000 + n.bit_length(), device=dev)
@@ -262,13 +264,28 @@ def sweep(args):
 def roofline_bound(w, kernel, peak_tflops):
     """(bound, algorithmic work per launch, peak, unit) of one timed kernel:
     HBM when its flops per algorithmic byte fall below the machine balance
-    (peak flops / HBM bandwidth), MFMA otherwise."""
+    (peak flops / HBM bandwidth), MFMA otherwise.
+
+    Algorithmic flops per admissible (query, key) pair of one head: the
+    forward 4 d (S1, S2).  The backward is credited 12 d in all: the two
+    recomputed score products (4 d) and the four gradient products (8 d).
+    Each of its two kernels forms two of the gradients, so each is credited
+    half of that, 6 d; the second recompute the two-kernel form executes is
+    not algorithmic work (see executed_flops)."""
     fwd_fl = w.fwd_flops()
-    flops = fwd_fl if kernel == "fwd" else 2 * fwd_fl
+    flops = fwd_fl if kernel == "fwd" else 1.5 * fwd_fl
     nbytes = w.fwd_bytes() if kernel == "fwd" else w.bwd_bytes(kernel)
     if flops / nbytes < peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
         return "hbm", nbytes, PEAK_HBM_GBS, "GB/s"
     return "mfma", flops, peak_tflops, "TFLOP/s"
+
+
+def executed_flops(w, kernel):
+    """MFMA flops one launch of the kernel executes: the forward's 4 d per
+    pair; each backward kernel recomputes both score blocks (4 d) and forms
+    two gradients (4 d), 8 d per pair."""
+    fwd_fl = w.fwd_flops()
+    return fwd_fl if kernel == "fwd" else 2 * fwd_fl
 
 
 def main():
@@ -337,13 +354,21 @@ def main():
     wall = time.perf_counter() - t0
     log(f"bench: {args.steps} timed steps done in {wall:.3f} s")
 
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    def median(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    # Per-step and per-kernel figures are medians over the timed steps (means
+    # are reported beside them).
     step_ev = sorted(e[0].elapsed_time(e[nev - 1]) for e in events)
-    step_ms = sum(step_ev) / args.steps
-    kern = {"fwd": fwd_ms}
+    step_ms = median(step_ev)
+    spans = {"fwd": (0, 1)}
     if do_bwd:
-        kern["bwd_dk"] = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-        kern["bwd_dq"] = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+        spans["bwd_dk"] = (1, 2)
+        spans["bwd_dq"] = (2, 3)
+    kern = {k: median(e[a].elapsed_time(e[b]) for e in events) for k, (a, b) in spans.items()}
+    kern_mean = {k: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps for k, (a, b) in spans.items()}
+    fwd_ms = kern["fwd"]
     ms_per_step = wall * 1e3 / args.steps
 
     fwd_fl = w.fwd_flops()
@@ -352,11 +377,10 @@ def main():
     value = total_fl / (step_ms * 1e-3) / 1e12
     fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
 
-    # Dominant kernel: the one with the largest average duration.  Its
-    # algorithmic work per launch: forward 4 N_Q N_K d flops per head; each
-    # backward kernel recomputes both score blocks (4) and forms two gradients
-    # (4): 8 N_Q N_K d.  Workloads below the machine balance (decoding rows)
-    # are priced in algorithmic HBM bytes against the HBM bandwidth instead.
+    # Dominant kernel: the one with the largest median duration, priced in
+    # algorithmic work per launch (roofline_bound).  Workloads below the
+    # machine balance (decoding rows) are priced in algorithmic HBM bytes
+    # against the HBM bandwidth instead.
     dom = max(kern, key=kern.get)
     bound, work, rpeak, runit = roofline_bound(w, dom, peak)
     scale_unit = 1e12 if runit == "TFLOP/s" else 1e9
@@ -365,6 +389,10 @@ def main():
             "frac": round(ach / rpeak, 4), "traffic": recorded_traffic(w.name, dom),
             ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work,
             "avg_launch_ms": round(kern[dom], 4)}
+    if bound == "mfma":
+        ex = executed_flops(w, dom)
+        roof["executed_flops_per_launch"] = ex
+        roof["executed_tflops"] = round(ex / (kern[dom] * 1e-3) / 1e12, 2)
 
     # The graphics clock, sampled while untimed steps keep the GPU busy (the
     # clock drops within milliseconds once the GPU idles).
@@ -407,11 +435,12 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "pct_peak_fwd": round(100 * fwd_tf / peak, 2),
         "pct_peak_fwdbwd": round(100 * value / peak, 2),
-        "event_ms_per_step": round(step_ms, 4),
-        "event_ms_median": round(step_ev[len(step_ev) // 2], 4),
+        "event_ms_median": round(step_ms, 4),
+        "event_ms_mean": round(sum(step_ev) / len(step_ev), 4),
         "event_ms_min": round(step_ev[0], 4),
         "observed_clock": clock,
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "kernel_ms_mean": {k: round(v, 4) for k, v in kern_mean.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

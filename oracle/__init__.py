@@ -5,8 +5,8 @@ CPU-baseline leg may import this package; the product path never does.  It
 shares no code with the HIP library (see ``streamkl_oracle.c`` for what it
 computes and which passages of the StreamKL summary page each step follows).
 
-``forward``/``forward_backward`` take numpy (or anything ``np.asarray``
-accepts) arrays shaped [..., N, d] for Q/K and return float64 arrays.
+``head`` takes the query and key rows of one attention head as numpy arrays
+(or anything ``np.asarray`` accepts) shaped [N, d] and returns float64 arrays.
 """
 import ctypes
 import os
@@ -84,22 +84,4 @@ def head(q1, k1, q2, k2, scale, causal, g=None, rows=None, grads=False, lib=None
                          _ptr(out.get("dq2")), _ptr(out.get("dk2")))
     if rc != 0:
         raise MemoryError("oracle scratch allocation failed")
-    return out
-
-
-def batch(q1, k1, q2, k2, scale, causal, g=None, grads=False, lib=None):
-    """All heads of [..., N, d] inputs; returns arrays with the leading dims."""
-    q1, k1, q2, k2 = _f64(q1), _f64(k1), _f64(q2), _f64(k2)
-    lead = q1.shape[:-2]
-    n_q, d = q1.shape[-2:]
-    n_k = k1.shape[-2]
-    nh = int(np.prod(lead)) if lead else 1
-    Q1, K1 = q1.reshape(nh, n_q, d), k1.reshape(nh, n_k, d)
-    Q2, K2 = q2.reshape(nh, n_q, d), k2.reshape(nh, n_k, d)
-    G = None if g is None else _f64(g).reshape(nh, n_q)
-    res = [head(Q1[h], K1[h], Q2[h], K2[h], scale, causal,
-                None if G is None else G[h], grads=grads, lib=lib) for h in range(nh)]
-    out = {}
-    for key in res[0]:
-        out[key] = np.stack([r[key] for r in res]).reshape(lead + res[0][key].shape)
     return out

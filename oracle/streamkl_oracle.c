@@ -183,29 +183,6 @@ int oracle_head(const double *q1, const double *k1, const double *q2,
   return failed ? -1 : 0;
 }
 
-/*
- * oracle_batch: every row of every head of a [B*H] batch.  Tensors are the
- * concatenation of per-head slabs (head stride n_q*d or n_k*d; row vectors
- * head stride n_q).  Gradient pointers NULL => forward only.
- */
-int oracle_batch(const double *q1, const double *k1, const double *q2,
-                 const double *k2, const double *g, int bh, int n_q, int n_k,
-                 int d, double scale, int causal, double *kl, double *lse1,
-                 double *lse2, double *dq1, double *dk1, double *dq2,
-                 double *dk2) {
-  const size_t qs = (size_t)n_q * d, ks = (size_t)n_k * d;
-  for (int h = 0; h < bh; ++h) {
-    int rc = oracle_head(
-        q1 + h * qs, k1 + h * ks, q2 + h * qs, k2 + h * ks,
-        g ? g + (size_t)h * n_q : NULL, n_q, n_k, d, scale, causal, 0, n_q,
-        kl + (size_t)h * n_q, lse1 + (size_t)h * n_q, lse2 + (size_t)h * n_q,
-        dq1 ? dq1 + h * qs : NULL, dk1 ? dk1 + h * ks : NULL,
-        dq2 ? dq2 + h * qs : NULL, dk2 ? dk2 + h * ks : NULL);
-    if (rc) return rc;
-  }
-  return 0;
-}
-
 /* Threads the OpenMP runtime will use for the next parallel region. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

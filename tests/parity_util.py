@@ -27,16 +27,47 @@ def row_tol(dtype):
     return (1e-5, 0.0) if dtype == torch.float32 else (2e-3, 1e-2)
 
 
-def check_rows(got, ref, dtype, what, mag=None):
+U32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+def score_roundings(dtype, d):
+    """fp32 roundings in one raw score s = <q, k> on the matrix cores: the
+    bf16 products (v_mfma_f32_32x32x16_bf16) add 16 exact products per
+    instruction into the fp32 accumulator, d / 16 instructions; the fp32
+    ones (v_mfma_f32_32x32x2_f32) add 2, d / 2 instructions."""
+    return d // 16 if dtype == torch.bfloat16 else d // 2
+
+
+def magnitude_k(dtype, d):
+    """Multiple of 2^-24 |LSE_ref| that bounds the kernels' fp32 rounding
+    error in KL, LSE1 and LSE2 when the logits are far from unit scale.
+
+    With n = score_roundings(dtype, d), each score carries at most n u M,
+    M the magnitude of its partial sums (about |LSE| on the rows these inputs
+    make).  LSE_t inherits one score error, plus one rounding each in the
+    exponent's shift -m c, in m * scale and in m * scale + log l, and the
+    same again through the lane-half merge: (n + 4) u |LSE|.  KL =
+    scale acc / l1 + LSE2 - LSE1 adds both LSE errors, the error of
+    acc / l1 (s1 - s2 carries two score errors, 2 n u |LSE|) and the two
+    roundings of the final sum on terms of size |LSE|, 2 u |LSE| each,
+    plus one for the division: 2 (n + 4) + 2 n + 5 = 4 n + 13."""
+    return 4 * score_roundings(dtype, d) + 13
+
+
+def check_rows(got, ref, dtype, what, mag=None, k=None):
     """got/ref: float64 arrays of per-row values; raise with the worst row.
 
-    ``mag``: per-row logit magnitude (max |LSE_ref|) for inputs far outside
-    the unit-scale workloads; the absolute bound then grows with it, since
-    fp32 score and LSE rounding errors are relative to the logits' size."""
+    The bound is the stated per-row tolerance: fp32 inputs 1e-5, bf16 inputs
+    2e-3 + 1e-2 |ref|.  ``mag`` (per-row max(|LSE1_ref|, |LSE2_ref|)) and
+    ``k`` add the fp32 rounding of logits far outside unit scale, k 2^-24 mag
+    with k from magnitude_k (or exact_score_k for inputs whose scores are
+    exact in fp32); ``k`` is required with ``mag``."""
     atol, rtol = row_tol(dtype)
     err = np.abs(got - ref)
-    scale = 1.0 if mag is None else np.maximum(1.0, np.abs(mag))
-    bound = atol * scale + rtol * np.abs(ref)
+    bound = atol + rtol * np.abs(ref)
+    if mag is not None:
+        assert k is not None, "a magnitude term needs its derived multiple"
+        bound = bound + k * U32 * np.abs(mag)
     bad = ~(err <= bound)
     if bad.any():
         i = int(np.argmax(np.where(bad, err - bound, -np.inf)))

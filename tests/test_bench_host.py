@@ -142,3 +142,23 @@ def test_roofline_bound_follows_arithmetic_intensity():
     n = 32768
     assert h.bwd_bytes("bwd_dk") == 32 * (2 * 2 * n * 128 * 2 + 16 * n + 2 * n * 128 * 2)
     assert h.fwd_bytes() == 32 * (2 * 2 * n * 128 * 2 + 12 * n)
+
+
+def test_roofline_credits_the_algorithmic_flops():
+    """Per admissible (query, key) pair of a head the forward is credited
+    4 d flops and each backward kernel 6 d (half of the backward's 12 d: two
+    recomputed score products and four gradient products); the second
+    recompute of the two-kernel form is reported as executed work only."""
+    sys.path.insert(0, ROOT)
+    import bench
+    h = WORKLOADS["h32k"]
+    pairs = 32 * 32768 * 32768 / 2
+    assert bench.roofline_bound(h, "fwd", 2500.0)[1] == 4 * 128 * pairs
+    for k in ("bwd_dk", "bwd_dq"):
+        assert bench.roofline_bound(h, k, 2500.0)[1] == 6 * 128 * pairs
+        assert bench.executed_flops(h, k) == 8 * 128 * pairs
+    # the two backward kernels together carry the backward's 12 d, and with
+    # the forward the 16 d of the headline figure
+    assert 2 * bench.roofline_bound(h, "bwd_dk", 2500.0)[1] + bench.roofline_bound(h, "fwd", 2500.0)[1] \
+        == h.fwdbwd_flops()
+    assert abs(bench.roofline_bound(h, "bwd_dk", 2500.0)[1] - 1.319e13) < 1e10

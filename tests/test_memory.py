@@ -23,14 +23,8 @@ def _round512(n):
     return (n + 511) // 512 * 512
 
 
-def test_sweep_needs_only_the_declared_workspace(capsys):
-    import bench
+def _check_rows(rows, H, d):
     from attention_distillation_kl_amd import _lib
-
-    H, d = 2, 128
-    bench.sweep(argparse.Namespace(sweep_max=8192, sweep_heads=H))
-    rows = [json.loads(line) for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
-    assert [r["N"] for r in rows] == [4096, 8192]
     for r in rows:
         n = r["N"]
         assert r["input_bytes"] == 4 * H * n * d * 2
@@ -43,7 +37,37 @@ def test_sweep_needs_only_the_declared_workspace(capsys):
                 ws = _lib.bwd_workspace_size(1, H, n, n, d, int(causal), _lib.BF16, mask)
                 assert r[f"bwd_{cfg}_extra_hbm_bytes_{tag}"] == _round512(ws), (n, tag, cfg)
             assert r[f"fwd_ms_{tag}"] > 0 and r[f"bwd_config1_ms_{tag}"] > 0
+
+
+def test_sweep_needs_only_the_declared_workspace(capsys):
+    import bench
+    from attention_distillation_kl_amd import _lib
+
+    H, d = 2, 128
+    bench.sweep(argparse.Namespace(sweep_min=4096, sweep_max=8192, sweep_heads=H))
+    rows = [json.loads(line) for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    assert [r["N"] for r in rows] == [4096, 8192]
+    _check_rows(rows, H, d)
     # At these sizes (2 heads) both the split-K forward and the partitioned
     # backward are chosen, so the workspace paths are the ones measured.
     assert _lib.fwd_splits(1, H, 4096, 4096, d, 1, _lib.BF16) > 1
     assert _lib.bwd_workspace_size(1, H, 4096, 4096, d, 1, _lib.BF16, 3) > 0
+
+
+def test_long_contexts_need_no_device_memory_beyond_outputs(capsys):
+    """16K and 32K tokens at the headline's 32 heads (a 32K causal attention
+    matrix of one head alone is 2 GiB in bf16, 64 GiB for all 32): every
+    forward and backward call needs exactly the memory of its inputs and
+    outputs, nothing else -- the grids fill the GPU, so no workspace either."""
+    import bench
+    from attention_distillation_kl_amd import _lib
+
+    H, d = 32, 128
+    bench.sweep(argparse.Namespace(sweep_min=16384, sweep_max=32768, sweep_heads=H))
+    rows = [json.loads(line) for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    assert [r["N"] for r in rows] == [16384, 32768]
+    _check_rows(rows, H, d)
+    for r in rows:
+        for key, v in r.items():
+            if "extra_hbm_bytes" in key:
+                assert v == 0, (r["N"], key, v)

@@ -9,6 +9,7 @@ import torch
 from attention_distillation_kl_amd import WORKLOADS, make_inputs, workload_inputs
 from attention_distillation_kl_amd import _lib, ops
 from attention_distillation_kl_amd.inputs import upstream_grad
+import oracle
 from parity_util import (check_grad, check_rows, head64, log, oracle_heads, oracle_row_blocks, to64)
 
 pytestmark = pytest.mark.gpu
@@ -138,10 +139,16 @@ def identities(q1, k1, q2, k2, gr, tag):
 
 @pytest.mark.parametrize("name", ["c3", "c5", "h32k"])
 def test_bwd_full_size(name):
-    """Full-size workloads in the benchmark's launch configuration.  Exact
-    oracle values are cheap for the first and last query rows (dQ) and, with
-    the causal mask, for the last keys (only the last rows reach them); the
-    rest is held to identities that hold at any size."""
+    """Full-size workloads in the benchmark's launch configuration.
+
+    The last head is compared whole with the oracle: KL, LSE1, LSE2 per row
+    and dQ1, dK1, dQ2, dK2 per (b, h) slice, and separately the key gradients
+    of the first 2048 keys, which (causal) take the longest query streams:
+    key block 0 accumulates over every query of the head.  The first head is
+    checked on its first and last query rows (dQ) and, causally, the last
+    keys (dK, reached only by the last rows); the rest of the batch is held to
+    identities that hold at any size.  The whole head costs the oracle about
+    10 s at 32K tokens and 40 s at 64K on 16 cores."""
     w = WORKLOADS[name]
     log(f"bwd {name} full size")
     q1, k1, q2, k2 = workload_inputs(w, DEV)
@@ -151,18 +158,31 @@ def test_bwd_full_size(name):
     identities(q1, k1, q2, k2, gr, name)
     nh = w.B * w.H
     tail = 32
-    for hh in (0, nh - 1):
-        b, h = divmod(hh, w.H)
-        h64 = head64(q1, k1, q2, k2, hh)
-        # last rows: exact dQ for them and, causally, exact dK for the last keys
-        ref = oracle_row_blocks(h64, w.scale, w.causal, [(w.NQ - tail, w.NQ)], grads=True)
-        for t in (1, 2):
-            check_grad(to64(gr[f"dq{t}"][b, h])[-tail:], ref[f"dq{t}"][-tail:], q1.dtype, f"{name} h{hh} dq{t} tail")
-            check_grad(to64(gr[f"dk{t}"][b, h])[-tail:], ref[f"dk{t}"][-tail:], q1.dtype, f"{name} h{hh} dk{t} tail")
-        ref = oracle_row_blocks(h64, w.scale, w.causal, [(0, tail)], grads=True)
-        for t in (1, 2):
-            check_grad(to64(gr[f"dq{t}"][b, h])[:tail], ref[f"dq{t}"][:tail], q1.dtype, f"{name} h{hh} dq{t} head")
-        check_rows(to64(kl[b, h])[:tail], ref["kl"][:tail], q1.dtype, f"{name} h{hh} kl")
+    hh = 0
+    b, h = divmod(hh, w.H)
+    h64 = head64(q1, k1, q2, k2, hh)
+    # last rows: exact dQ for them and, causally, exact dK for the last keys
+    ref = oracle_row_blocks(h64, w.scale, w.causal, [(w.NQ - tail, w.NQ)], grads=True)
+    for t in (1, 2):
+        check_grad(to64(gr[f"dq{t}"][b, h])[-tail:], ref[f"dq{t}"][-tail:], q1.dtype, f"{name} h{hh} dq{t} tail")
+        check_grad(to64(gr[f"dk{t}"][b, h])[-tail:], ref[f"dk{t}"][-tail:], q1.dtype, f"{name} h{hh} dk{t} tail")
+    ref = oracle_row_blocks(h64, w.scale, w.causal, [(0, tail)], grads=True)
+    for t in (1, 2):
+        check_grad(to64(gr[f"dq{t}"][b, h])[:tail], ref[f"dq{t}"][:tail], q1.dtype, f"{name} h{hh} dq{t} head")
+    check_rows(to64(kl[b, h])[:tail], ref["kl"][:tail], q1.dtype, f"{name} h{hh} kl")
+    # the last head, whole
+    hh = nh - 1
+    b, h = divmod(hh, w.H)
+    log(f"bwd {name}: oracle on head {hh}, all {w.NQ} rows")
+    ref = oracle.head(*head64(q1, k1, q2, k2, hh), w.scale, w.causal, grads=True)
+    for key, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
+        check_rows(to64(got[b, h]), ref[key], q1.dtype, f"{name} h{hh} {key} (whole head)")
+    for n in NAMES:
+        check_grad(to64(gr[n][b, h]), ref[n], q1.dtype, f"{name} h{hh} {n} (whole head)")
+    for t in (1, 2):
+        first = min(2048, w.NK)
+        check_grad(to64(gr[f"dk{t}"][b, h])[:first], ref[f"dk{t}"][:first], q1.dtype,
+                   f"{name} h{hh} dk{t} first {first} keys")
     del q1, k1, q2, k2, gr
     torch.cuda.empty_cache()
 

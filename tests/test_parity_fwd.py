@@ -8,7 +8,8 @@ import torch
 
 from attention_distillation_kl_amd import WORKLOADS, make_inputs, workload_inputs
 from attention_distillation_kl_amd import ops
-from parity_util import (check_rows, head64, log, oracle_heads, oracle_row_blocks, row_blocks, to64)
+from parity_util import (check_rows, head64, log, magnitude_k, oracle_heads, oracle_row_blocks, row_blocks,
+                         to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,18 +17,26 @@ DEV = "cuda"
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def run_and_compare(q1, k1, q2, k2, scale, causal, heads=None, tag="", by_magnitude=False):
+def run_and_compare(q1, k1, q2, k2, scale, causal, heads=None, tag="", by_magnitude=False, k=None,
+                    tol_dtype=None):
+    """Forward through the C ABI against the oracle, row by row.  With
+    ``by_magnitude`` the bound adds k 2^-24 max(|LSE1_ref|, |LSE2_ref|), k
+    from magnitude_k unless given; ``tol_dtype`` overrides the dtype whose
+    stated tolerance applies."""
     kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
     torch.cuda.synchronize()
     B, H = q1.shape[:2]
     heads = range(B * H) if heads is None else heads
     ref = oracle_heads(q1, k1, q2, k2, scale, causal, heads)
+    if by_magnitude and k is None:
+        k = magnitude_k(q1.dtype, q1.shape[-1])
+    tdt = q1.dtype if tol_dtype is None else tol_dtype
     worst = 0.0
     for hh in heads:
         b, h = divmod(hh, H)
         mag = np.maximum(np.abs(ref[hh]["lse1"]), np.abs(ref[hh]["lse2"])) if by_magnitude else None
         for name, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
-            worst = max(worst, check_rows(to64(got[b, h]), ref[hh][name], q1.dtype, f"{tag} head {hh} {name}", mag))
+            worst = max(worst, check_rows(to64(got[b, h]), ref[hh][name], tdt, f"{tag} head {hh} {name}", mag, k))
     return kl, l1, l2, worst
 
 
@@ -119,7 +128,9 @@ def test_fwd_uniform_student():
 def test_fwd_peaked_and_large_inputs(dt):
     """scale = 1 on N(0, 1) d = 128 data gives logits with std ~11 (near one-hot
     rows); x8 inputs on top of that stress the max-shift.  Logits reach tens
-    to hundreds here, so the fp32 bound is taken relative to max |LSE|."""
+    to hundreds here, so the bound adds the fp32 rounding of scores of that
+    size (parity_util.magnitude_k: 45 u |LSE| for bf16, 269 u |LSE| for fp32
+    at d = 128)."""
     q1, k1, q2, k2 = make_inputs(1, 2, 256, 256, 128, DT[dt], "student", 0.3, seed=8, device=DEV)
     kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, True, tag="peaked", by_magnitude=True)
     assert torch.isfinite(kl).all()
@@ -136,8 +147,8 @@ def test_fwd_logits_that_rise_or_fall_along_the_keys(dt, direction, causal):
     every row grow (direction 1) by about 1.5 per key, i.e. by more than 64
     log2 units per 32-key block, so the running shift must be raised on
     every block; or they fall (direction -1), so the first block's maximum
-    holds for the whole row.  The bound is relative to |LSE| as for the
-    other inputs far outside unit scale."""
+    holds for the whole row.  The bound adds the fp32 rounding of scores of
+    that size, as for the other inputs far outside unit scale."""
     g = torch.Generator(device=DEV).manual_seed(77)
     NQ, NK, d = 96, 700, 64
     u = torch.randn(d, device=DEV, generator=g)
@@ -152,6 +163,58 @@ def test_fwd_logits_that_rise_or_fall_along_the_keys(dt, direction, causal):
     q1, k1, q2, k2 = (x[None, None].to(DT[dt]).contiguous() for x in (queries(), keys(), queries(), keys()))
     kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, causal, tag=f"ramp {direction}", by_magnitude=True)
     assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
+
+
+# KL / LSE rounding when every score is exact in fp32 (multiple of 2^-24
+# |LSE_ref|).  Left: one rounding each in the exponent's shift -m c, in
+# m * scale, in m * scale + log l and in the lane-half merge; the raises'
+# rescale factors exp2((m - m') c), whose arguments sum to at most 2 |LSE|
+# over a row: 6 per LSE.  KL adds both LSEs, the weights of acc / l1 (2)
+# and the final sum and division (5): 12 + 2 + 5 = 19, taken as 20.
+EXACT_SCORE_K = 20
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_raised_shifts_with_exact_scores(dt, direction, causal):
+    """The shift-raising path with no score rounding in the way.  Every input
+    is a multiple of 1/8 below 32 in magnitude (exact in bf16), so every
+    product is a multiple of 1/64 and every dot product (|s| < 2^17) is exact
+    in fp32, on both matrix-core paths.  Queries are 24 along axis 0 and keys
+    climb (or fall) by 1/8 per key along it: the logits move by 3 per key,
+    about 138 log2 units per 32-key block, so each block forces a raise of
+    the running shift (or, falling, the first block's maximum holds).  The
+    error left is the rounding of the shifts, rescales and finalisation,
+    bounded by EXACT_SCORE_K 2^-24 |LSE| on top of the fp32 tolerance of
+    1e-5 for both dtypes: about 1e-3 at |LSE| ~ 765, so a rescale of l or
+    acc off by more than that fails (the earlier bounds for such logits were
+    1e-2 in fp32 and 1.5 in bf16)."""
+    g = torch.Generator(device="cpu").manual_seed(91)
+    NQ, NK, d = 80, 256, 64
+    ramp = torch.arange(NK, dtype=torch.float32) / 8.0
+    if direction < 0:
+        ramp = ramp.flip(0)
+
+    def eighths(n, lim):
+        return torch.randint(-lim, lim + 1, (n, d), generator=g).float() / 8.0
+
+    def keys():
+        k = eighths(NK, 8)
+        k[:, 0] = ramp
+        return k
+
+    def queries():
+        q = eighths(NQ, 8)
+        q[:, 0] = 24.0
+        return q
+
+    q1, k1, q2, k2 = (x[None, None].to(DEV).to(DT[dt]).contiguous() for x in (queries(), keys(), queries(), keys()))
+    for x in (q1, k1, q2, k2):   # the values survived the cast unchanged
+        assert torch.equal(x.float().cpu() * 8, (x.float().cpu() * 8).round())
+    kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, causal, tag=f"exact ramp {direction}",
+                                    by_magnitude=True, k=EXACT_SCORE_K, tol_dtype=torch.float32)
+    assert l1.abs().max() > 500      # the logits really are far from unit scale
 
 
 def test_fwd_is_deterministic():
