@@ -13,7 +13,10 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 GRAD_Q1K1, GRAD_Q2K2, GRAD_ALL = 1, 2, 3
 
+NOALLOC_SCRATCH_BYTES = 16 << 20   # STREAMKL_NOALLOC_SCRATCH_BYTES
+
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splits", "streamkl_fwd_workspace_size", "streamkl_fwd_splitk",
+           "streamkl_fwd_splitk_noalloc",
            "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dq_ws", "streamkl_bwd_dk",
            "streamkl_bwd_workspace_size", "streamkl_status_str", "streamkl_abi_version")
 
@@ -47,6 +50,9 @@ def load(path: str = LIB_PATH):
     lib.streamkl_fwd_splitk.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
                                         _fp, _fp, _fp, _vp, _sz, _vp]
     lib.streamkl_fwd_splitk.restype = _i
+    lib.streamkl_fwd_splitk_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i,
+                                                _fp, _fp, _fp, _vp]
+    lib.streamkl_fwd_splitk_noalloc.restype = _i
     lib.streamkl_bwd.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
                                  _f, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.streamkl_bwd.restype = _i
@@ -96,6 +102,13 @@ def fwd_splitk(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits, kl
                workspace, workspace_bytes, stream):
     return load().streamkl_fwd_splitk(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits,
                                       kl, lse1, lse2, workspace, workspace_bytes, stream)
+
+
+def fwd_splitk_noalloc(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits, kl, lse1, lse2, stream):
+    """streamkl_fwd_splitk_noalloc: the split-K forward with the library's
+    fixed device scratch array instead of a caller's workspace."""
+    return load().streamkl_fwd_splitk_noalloc(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, splits,
+                                              kl, lse1, lse2, stream)
 
 
 def bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,

@@ -1,11 +1,14 @@
 // streamkl_api.hip -- the C ABI declared in include/streamkl.h: argument
 // validation, then dispatch to the forward / backward kernels.  No device
-// memory is allocated here and no state is kept between calls.
+// memory is allocated here.  The only state kept between calls is the
+// per-device address of the fixed scratch array of
+// streamkl_fwd_splitk_noalloc, looked up on its first call on a device.
 #include "streamkl.h"
 #include "streamkl_launch.h"
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 namespace {
 
@@ -227,3 +230,59 @@ streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc
+// Partition states of streamkl_fwd_splitk_noalloc: a fixed array in device
+// memory, one copy per GPU, alive until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) float scratch[STREAMKL_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` per device
+
+// Device address of `scratch` on the calling thread's current device, or
+// nullptr if the runtime cannot tell the device or resolve the symbol.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" streamkl_status streamkl_fwd_splitk_noalloc(const void *q1, const void *k1, const void *q2,
+                                                       const void *k2, int B, int H, int N_Q, int N_K, int d,
+                                                       float scale, int causal, int dtype, int splits, float *kl,
+                                                       float *lse1, float *lse2, void *stream) {
+  streamkl_status s = check_common(q1, k1, q2, k2, B, H, N_Q, N_K, d, scale, causal, dtype);
+  if (s != STREAMKL_OK) return s;
+  if (splits < 1 || splits > STREAMKL_MAX_SPLITS) return STREAMKL_ERR_INVALID_ARGUMENT;
+  const long long rows = (long long)B * H * N_Q;
+  if (!row_vec_ok(kl, rows) || !row_vec_ok(lse1, rows) || !row_vec_ok(lse2, rows))
+    return STREAMKL_ERR_INVALID_ARGUMENT;
+  const size_t need = streamkl_fwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, splits);
+  if (need > STREAMKL_NOALLOC_SCRATCH_BYTES) return STREAMKL_ERR_WORKSPACE;
+  if (rows == 0) return STREAMKL_OK;
+  streamkl::FwdArgs a{q1, k1, q2, k2, kl, lse1, lse2, B * H, N_Q, N_K, d, scale, causal != 0,
+                      dtype == STREAMKL_BF16};
+  a.splits = splits;
+  if (splits > 1) {
+    // Every (partition, row) state the merge reads is written by the split
+    // kernel of the same call, so nothing needs clearing first.
+    a.part = static_cast<float *>(scratch_on_current_device());
+    if (!a.part) return STREAMKL_ERR_HIP;
+  }
+  return streamkl::launch_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
+                                                                                  : STREAMKL_ERR_HIP;
+}

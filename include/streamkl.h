@@ -35,8 +35,10 @@
  *            mask is aligned to the bottom-right corner (j <= i when
  *            N_Q == N_K).  Requires N_Q <= N_K so every row has a key.
  *  Pointers  every tensor pointer is a DEVICE pointer owned by the caller and
- *            must be 16-byte aligned.  The library never allocates, frees or
- *            keeps device memory and holds no global mutable state.  Outputs
+ *            must be 16-byte aligned.  The library never allocates or frees
+ *            device memory; apart from the fixed scratch array of
+ *            streamkl_fwd_splitk_noalloc (and the cached per-device address
+ *            of it) it keeps none and holds no global mutable state.  Outputs
  *            are fully overwritten and must not alias inputs.
  *  Streams   `stream` is a hipStream_t (NULL = the default stream).  Work is
  *            enqueued asynchronously; nothing synchronises the host.
@@ -136,6 +138,39 @@ streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1,
                                     int splits, float *kl, float *lse1,
                                     float *lse2, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* Size of the fixed device scratch array of streamkl_fwd_splitk_noalloc. */
+#define STREAMKL_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * streamkl_fwd_splitk_noalloc -- streamkl_fwd_splitk for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * (e.g. decoding rows over long key sets), harnesses that forbid hipMalloc.
+ * It takes no workspace and allocates nothing: the partition states live in
+ * a fixed array of STREAMKL_NOALLOC_SCRATCH_BYTES in device memory, one copy
+ * per GPU, created when the library's code is loaded on that GPU and held
+ * until the process ends.  The array is the one of the calling thread's
+ * current device, which must be the device of `stream` and of the tensors;
+ * its address is looked up on the first call on each device.
+ *   Arguments, results and errors as streamkl_fwd_splitk (bitwise the same
+ *   results for the same `splits`), without workspace / workspace_bytes.
+ *   STREAMKL_ERR_WORKSPACE when streamkl_fwd_workspace_size(...) for these
+ *   arguments exceeds STREAMKL_NOALLOC_SCRATCH_BYTES (5 * splits * B*H*N_Q
+ *   floats must fit: e.g. 32 heads of 2048 queries at 16 partitions); a
+ *   failed address lookup returns STREAMKL_ERR_HIP.
+ * Every call on one GPU uses that GPU's one array, and a call leaves its
+ * partition states there.  Calls on one GPU whose work may overlap (two
+ * streams, or two host threads) race on it and give wrong results: order
+ * them on one stream or with events.  Nothing needs clearing between calls:
+ * each call writes every state it reads.
+ */
+streamkl_status streamkl_fwd_splitk_noalloc(const void *q1, const void *k1,
+                                            const void *q2, const void *k2,
+                                            int B, int H, int N_Q, int N_K,
+                                            int d, float scale, int causal,
+                                            int dtype, int splits, float *kl,
+                                            float *lse1, float *lse2,
+                                            void *stream);
 
 /*
  * streamkl_bwd_workspace_size -- bytes of device workspace streamkl_bwd needs

@@ -140,6 +140,36 @@ def test_fwd_splitk_single_partition_needs_no_workspace(lib, no_gpu):
     assert fwd_splitk(splits=1, ws=None, wsb=0) == _lib.ERR_HIP
 
 
+def fwd_splitk_noalloc(**kw):
+    a = dict(q1=A, k1=A2, q2=A3, k2=A4, B=1, H=2, NQ=64, NK=4096, d=128, scale=0.125, causal=0,
+             dtype=_lib.BF16, splits=4, kl=O1, lse1=O2, lse2=O3, stream=None)
+    a.update(kw)
+    return _lib.fwd_splitk_noalloc(a["q1"], a["k1"], a["q2"], a["k2"], a["B"], a["H"], a["NQ"], a["NK"], a["d"],
+                                   a["scale"], a["causal"], a["dtype"], a["splits"], a["kl"], a["lse1"],
+                                   a["lse2"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(splits=0), INV), (dict(splits=1025), INV), (dict(d=96), UNS), (dict(scale=0.0), INV),
+    (dict(kl=None), INV), (dict(NQ=65, NK=64, causal=1), INV),
+    # 5 * 64 * 32 * 2048 floats = 80 MiB of partition states: beyond the fixed scratch
+    (dict(H=32, NQ=2048, NK=65536, splits=64), _lib.ERR_WORKSPACE),
+])
+def test_fwd_splitk_noalloc_rejects_bad_arguments(lib, kw, status):
+    assert fwd_splitk_noalloc(**kw) == status
+
+
+def test_fwd_splitk_noalloc_scratch_limit(lib, no_gpu):
+    """The largest problem whose partition states fit the fixed scratch array
+    passes validation (and, with no GPU here, fails at the device lookup);
+    one more query row per head does not fit."""
+    per_row = 5 * 4 * 4                       # five fp32 states, four partitions
+    nq = _lib.NOALLOC_SCRATCH_BYTES // per_row // 2
+    assert fwd_splitk_noalloc(NQ=nq) == _lib.ERR_HIP
+    assert fwd_splitk_noalloc(NQ=nq + 1) == _lib.ERR_WORKSPACE
+    assert fwd_splitk_noalloc(NQ=0) == _lib.OK          # nothing to do
+
+
 def test_default_split_choice(lib):
     # short query block over long keys: split; a grid that fills the GPU: not
     assert _lib.fwd_splits(1, 32, 2048, 65536, 128, 0, _lib.BF16) > 1
