@@ -31,9 +31,13 @@ _lib = None
 _vp, _fp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
 
-def load(path: str = LIB_PATH):
-    """Open the library (once) and declare the exported signatures."""
+def load(path: str = None):
+    """Open the library (once) and declare the exported signatures.  ``path``
+    defaults to LIB_PATH, read at the call (so a test can point the binding
+    at another build of the same sources)."""
     global _lib
+    if path is None:
+        path = LIB_PATH
     if _lib is not None and path == LIB_PATH:
         return _lib
     if not os.path.exists(path):
