@@ -18,7 +18,8 @@ NOALLOC_SCRATCH_BYTES = 16 << 20   # STREAMKL_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splits", "streamkl_fwd_workspace_size", "streamkl_fwd_splitk",
            "streamkl_fwd_splitk_noalloc",
            "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dq_ws", "streamkl_bwd_dk",
-           "streamkl_bwd_workspace_size", "streamkl_status_str", "streamkl_abi_version")
+           "streamkl_bwd_workspace_size", "streamkl_bwd_fused", "streamkl_bwd_fused_workspace_size",
+           "streamkl_bwd_fused_selected", "streamkl_status_str", "streamkl_abi_version")
 
 
 class StreamKLError(RuntimeError):
@@ -70,6 +71,12 @@ def load(path: str = None):
     lib.streamkl_bwd_dq_ws.restype = _i
     lib.streamkl_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
     lib.streamkl_bwd_workspace_size.restype = _sz
+    lib.streamkl_bwd_fused.argtypes = lib.streamkl_bwd.argtypes
+    lib.streamkl_bwd_fused.restype = _i
+    lib.streamkl_bwd_fused_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    lib.streamkl_bwd_fused_workspace_size.restype = _sz
+    lib.streamkl_bwd_fused_selected.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+    lib.streamkl_bwd_fused_selected.restype = _i
     lib.streamkl_status_str.argtypes = [_i]
     lib.streamkl_status_str.restype = ctypes.c_char_p
     lib.streamkl_abi_version.argtypes = []
@@ -139,3 +146,19 @@ def bwd_dq_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causa
 
 def bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask):
     return load().streamkl_bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask)
+
+
+def bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
+              dq1, dk1, dq2, dk2, workspace, workspace_bytes, stream):
+    """streamkl_bwd_fused: the single-pass backward with atomic query gradients."""
+    return load().streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype,
+                                     grad_mask, dq1, dk1, dq2, dk2, workspace, workspace_bytes, stream)
+
+
+def bwd_fused_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask):
+    return load().streamkl_bwd_fused_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask)
+
+
+def bwd_fused_selected(B, H, NQ, NK, d, causal, dtype, grad_mask):
+    """1 where streamkl_bwd runs the single-pass (fused) backward."""
+    return load().streamkl_bwd_fused_selected(B, H, NQ, NK, d, causal, dtype, grad_mask)

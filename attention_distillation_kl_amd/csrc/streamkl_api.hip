@@ -115,12 +115,39 @@ int bwd_dq_splits(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mas
 
 }  // namespace
 
-size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype,
-                                   int grad_mask) {
-  (void)causal;
+namespace {
+
+// Workspace of the query-gradient half with key partitions (0 without).
+size_t partitioned_ws_bytes(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
   const int s = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
   if (s <= 1) return 0;
   return streamkl::bwd_dq_workspace_floats(B * H, N_Q, d, grad_mask, s) * sizeof(float);
+}
+
+// Combined L2 of the eight XCDs (4 MiB each).
+constexpr size_t kL2Bytes = size_t(32) << 20;
+
+}  // namespace
+
+int streamkl_bwd_fused_selected(int B, int H, int N_Q, int N_K, int d, int causal, int dtype, int grad_mask) {
+  if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return 0;
+  if (dtype != STREAMKL_BF16 || grad_mask < 1 || grad_mask > 3 || (long long)B * H > INT32_MAX) return 0;
+  if (causal && N_Q > N_K) return 0;
+  // Short query blocks only, where the fused form measured faster than the
+  // two-kernel form: up to one 64-row query tile per head at d = 128 (slower
+  // from 96 queries); at d = 64, whose dQ products add twice the atomics per
+  // flop, up to 8 queries (slower at 32).  And the fp32 query-gradient buffer
+  // within L2, the page's criterion.
+  if (N_Q > (d == 128 ? 64 : 8)) return 0;
+  return streamkl::bwd_fused_workspace_floats(B * H, N_Q, d, grad_mask) * sizeof(float) <= kL2Bytes ? 1 : 0;
+}
+
+size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype,
+                                   int grad_mask) {
+  const size_t part = partitioned_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask);
+  if (!streamkl_bwd_fused_selected(B, H, N_Q, N_K, d, causal, dtype, grad_mask)) return part;
+  const size_t fused = streamkl::bwd_fused_workspace_floats(B * H, N_Q, d, grad_mask) * sizeof(float);
+  return fused > part ? fused : part;  // enough for streamkl_bwd_dq_ws as well
 }
 
 namespace {
@@ -157,7 +184,8 @@ bool bwd_is_noop(int B, int H, int N_Q, int N_K) { return (long long)B * H == 0 
 // kernel to key partitions whose partial sums go to the workspace.
 streamkl_status attach_dq_workspace(streamkl::BwdArgs &a, int B, int H, int N_Q, int N_K, int d, int causal,
                                     int dtype, int grad_mask, void *workspace, size_t workspace_bytes) {
-  const size_t need = streamkl_bwd_workspace_size(B, H, N_Q, N_K, d, causal, dtype, grad_mask);
+  (void)causal;
+  const size_t need = partitioned_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask);
   if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
   if (need > 0) {
     a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
@@ -173,6 +201,9 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2, con
                              int B, int H, int N_Q, int N_K, int d, float scale, int causal, int dtype,
                              int grad_mask, void *dq1, void *dk1, void *dq2, void *dk2, void *workspace,
                              size_t workspace_bytes, void *stream) {
+  if (streamkl_bwd_fused_selected(B, H, N_Q, N_K, d, causal, dtype, grad_mask))
+    return streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal, dtype,
+                              grad_mask, dq1, dk1, dq2, dk2, workspace, workspace_bytes, stream);
   streamkl::BwdArgs a;
   streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
                                   dtype, grad_mask, dq1, dk1, dq2, dk2, true, true, a);
@@ -227,6 +258,33 @@ streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2, 
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
   return streamkl::launch_bwd_dk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
                                                                                      : STREAMKL_ERR_HIP;
+}
+
+size_t streamkl_bwd_fused_workspace_size(int B, int H, int N_Q, int N_K, int d, int causal, int dtype,
+                                         int grad_mask) {
+  (void)N_K, (void)causal;
+  if (B <= 0 || H <= 0 || N_Q <= 0 || (d != 64 && d != 128) || dtype != STREAMKL_BF16) return 0;
+  if (grad_mask < 1 || grad_mask > 3 || (long long)B * H > INT32_MAX) return 0;
+  return streamkl::bwd_fused_workspace_floats(B * H, N_Q, d, grad_mask) * sizeof(float);
+}
+
+streamkl_status streamkl_bwd_fused(const void *q1, const void *k1, const void *q2, const void *k2,
+                                   const float *kl, const float *lse1, const float *lse2, const float *dkl,
+                                   int B, int H, int N_Q, int N_K, int d, float scale, int causal, int dtype,
+                                   int grad_mask, void *dq1, void *dk1, void *dq2, void *dk2, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  streamkl::BwdArgs a;
+  streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
+                                  dtype, grad_mask, dq1, dk1, dq2, dk2, true, true, a);
+  if (s != STREAMKL_OK) return s;
+  if (dtype != STREAMKL_BF16) return STREAMKL_ERR_UNSUPPORTED;
+  const size_t need = streamkl_bwd_fused_workspace_size(B, H, N_Q, N_K, d, causal, dtype, grad_mask);
+  if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
+  if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
+  return streamkl::launch_bwd_fused(a, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? STREAMKL_OK
+             : STREAMKL_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,520 @@
+// streamkl_bwd_fused.hip -- single-pass recompute backward with query
+// gradients added by atomics (gfx950, bf16 inputs).
+//
+// StreamKL summary page (gist.science 2606.20005), "Strategia di Ricalcolo",
+// kernel-fusion bullet: the backward visits each (query tile, key tile) pair
+// once, keeping dK in registers and adding dQ into a buffer with atomic adds
+// while that buffer fits in L2; where it does not, two separate kernels are
+// used (the separate-kernel form lives in streamkl_bwd.h).  "Risultati
+// Sperimentali", ablation bullet: the fused form pays off for short query
+// blocks.  The arithmetic is the recompute of the separate-kernel form:
+//   P1 = exp2(s1' c), s1' = s1 - LSE1/scale;   s2'' = s2 + (KL - LSE2)/scale
+//   P2 = exp2(s2'' c - KL c/scale)
+//   e2 = g (P2 - P1)                    (dS2 = e2)
+//   e1 = g P1 (s1' - s2'')              (dS1 = scale e1)
+//   dK_t = f_t e_t^T Q_t,  dQ_t = f_t e_t K_t,  f1 = scale^2, f2 = scale
+// with s_t the raw dot products and c = scale log2(e).
+//
+// Mapping:
+//   * a workgroup owns 128 key rows, one wave per 32 ("stationary"), and
+//     streams 64-row query tiles from its causal frontier to N_Q through LDS
+//     (direct global->LDS copies, double buffered, XOR-swizzled rows);
+//   * per 32-query block each wave recomputes S1^T, S2^T for its keys
+//     (queries from LDS as A operand, its keys in registers as B operand: a
+//     lane owns one key and 16 queries), forms e1, e2, adds dK_t^T += Q_t^T e_t
+//     (Q_t^T by transposing LDS reads), and stores e_t as bf16 into an LDS
+//     buffer laid out [key][query];
+//   * after a barrier, wave w forms dQ_t for one 32-column slice of d
+//     (mb = w % (d/32)) over the keys of its key group (all 128 at d = 128,
+//     64 at d = 64): dQ_t block (32 queries x 32 columns) = e_t (from the
+//     buffer, transposing reads) x K_t (fragments read once from the
+//     stationary tile at the start).  The sum over the workgroup's keys is
+//     thus formed on the matrix cores, and each lane adds 16 values per block
+//     and gradient with fp32 atomics; for one register the 64 lanes cover 32
+//     consecutive columns of two rows, i.e. two 128-byte lines;
+//   * the fp32 buffer is zeroed by a fill kernel before and converted to the
+//     gradient's element type (times f_t) by a second kernel after.
+// The order of the atomic additions varies from run to run, so dQ is not
+// bitwise reproducible (dK is).
+#include "streamkl_device.h"
+#include "streamkl_launch.h"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <type_traits>
+
+namespace streamkl {
+namespace {
+
+template <int D>
+struct FusedCfg {
+  using G = RowGeom<true, D>;
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBS = 32 * kWaves;                  // stationary keys per workgroup
+  static constexpr int kBT = 64;                           // streamed queries per tile
+  static constexpr int kSub = kBT / 32;                    // 32-query blocks per tile
+  static constexpr int kMB = D / 32;                       // 32-column slices of d
+  static constexpr int kGroups = kWaves / kMB;             // key groups of the dQ products
+  static constexpr int kGroupKeys = kBS / kGroups;         // keys per group: 128 (d = 128), 64 (d = 64)
+  static constexpr int kKSteps = kGroupKeys / 16;          // 16-key steps of a dQ product
+  static constexpr int kTileChunks = kBT * G::kChunks;     // 16-byte chunks per query tile and tensor
+  static constexpr int kLoads = kTileChunks / kThreads;    // copies per thread per tensor
+  static constexpr int kXChunks = kBS * G::kChunks;        // stationary tile, per tensor
+  static constexpr int kXLoads = kXChunks / kThreads;
+  static constexpr int kERowBytes = kBT * 2;               // one key's e row: 64 bf16
+  static constexpr int kEBytes = kBS * kERowBytes;         // e buffer, per tensor
+  // LDS (bytes): row constants of both stages, two query stages (Q1, Q2),
+  // the e buffers (e1, e2).  The stationary tiles (K1, K2) are needed only
+  // at the start; they share the space of stage 1 and the e buffers.
+  static constexpr int kCstBytes = 2 * 4 * kBT * 4;
+  static constexpr int kStageBytes = 2 * kTileChunks * 16;
+  static constexpr int kOffStage0 = kCstBytes;
+  static constexpr int kOffStage1 = kOffStage0 + kStageBytes;
+  static constexpr int kOffE = kOffStage1 + kStageBytes;
+  static constexpr int kOffX = kOffStage1;
+  static constexpr int kLdsBytes = kOffE + 2 * kEBytes;
+  static_assert(kOffX + 2 * kXChunks * 16 <= kLdsBytes, "stationary tiles must fit the shared space");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kTileChunks % kThreads == 0 && kXChunks % kThreads == 0, "tiles split evenly");
+  static_assert(kWaves % kMB == 0, "d slices split the waves evenly");
+};
+
+struct FusedParams {
+  const char *q1, *k1, *q2, *k2;
+  const float *kl, *lse1, *lse2, *dkl;
+  char *dk1, *dk2;
+  float *ws1, *ws2;   // fp32 query-gradient sums [bh][N_Q][d], zero on entry
+  int nq, nk, nsb;    // nsb: stationary blocks per head
+  float scale, c, inv_scale;
+};
+
+// Byte offset of (key, query) in an e buffer: rows of 64 bf16, 16-byte
+// chunks XOR-swizzled by the key's low three bits.  A transposing read takes
+// 4 consecutive queries (8 bytes, inside one chunk) from each of 8 keys, and
+// a store writes 4 consecutive queries for 32 keys: both spread over all
+// banks.
+__device__ __forceinline__ int ebyte(int key, int q) {
+  return key * 128 + (((q >> 3) ^ (key & 7)) << 4) + (q & 7) * 2;
+}
+
+template <int D, bool CAUSAL, int MASK, bool GSIGN>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void fused_bwd_kernel(FusedParams p) {
+  using C = FusedCfg<D>;
+  using G = typename C::G;
+  constexpr bool kG1 = (MASK & 1) != 0;
+  constexpr bool kG2 = (MASK & 2) != 0;
+  constexpr int kMB = C::kMB;
+  extern __shared__ u32x4 lds[];
+  char *lbase = reinterpret_cast<char *>(lds);
+  float (*cstage)[4 * C::kBT] = reinterpret_cast<float (*)[4 * C::kBT]>(lbase);
+  u32x4 *ystage0 = reinterpret_cast<u32x4 *>(lbase + C::kOffStage0);
+  u32x4 *ystage1 = reinterpret_cast<u32x4 *>(lbase + C::kOffStage1);
+  char *ebuf = lbase + C::kOffE;  // [tensor][key][query] bf16, swizzled
+  u32x4 *xtile = reinterpret_cast<u32x4 *>(lbase + C::kOffX);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int s16 = lane & 15, grp = lane >> 4;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = bid / p.nsb;
+  const int sblk = bid - bh * p.nsb;  // key block 0 first: with the mask it sees the most queries
+  const int s0 = sblk * C::kBS;
+  const int w0 = s0 + wave * 32;
+  const int srow = w0 + col;           // the lane's key
+  const int off = p.nk - p.nq;
+
+  const size_t koff = size_t(bh) * p.nk * G::kRowBytes;
+  const char *Y1 = p.q1 + size_t(bh) * p.nq * G::kRowBytes;
+  const char *Y2 = p.q2 + size_t(bh) * p.nq * G::kRowBytes;
+
+  // Streamed query range: from the workgroup's causal frontier to N_Q.
+  const int t_begin = CAUSAL ? max(0, s0 - off) : 0;
+  const int tile0 = t_begin / C::kBT;
+  const int tile1 = (p.nq + C::kBT - 1) / C::kBT;
+  const int ntiles = max(tile1 - tile0, 0);
+  // First admissible query of the lane's key, and whether its key exists.
+  const int lim = CAUSAL ? max(srow - off, 0) : 0;
+  const bool keys_past_end = w0 + 31 >= p.nk;  // wave-uniform
+
+  // Stationary key tiles -> LDS (rows past N_K repeat the last one; their e
+  // values are zero).  The score products' key fragments and the dQ
+  // products' key columns are both read from them, so each key row is
+  // fetched from memory once.
+  {
+    const char *K1 = p.k1 + koff, *K2 = p.k2 + koff;
+#pragma unroll
+    for (int i = 0; i < C::kXLoads; ++i) {
+      const int pos = i * C::kThreads + tid;
+      const int row = pos / G::kChunks;
+      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+      const size_t o = size_t(min(s0 + row, p.nk - 1)) * G::kRowBytes + ch * 16;
+      dma16(K1 + o, xtile + i * C::kThreads + wave * 64);
+      dma16(K2 + o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
+    }
+  }
+
+  auto issue = [&](int tile, int stage) {
+    u32x4 *wbase = (stage ? ystage1 : ystage0) + wave * 64;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int pos = i * C::kThreads + tid;
+      const int row = pos / G::kChunks;
+      const int ch = swz<G::kChunks>(row, pos % G::kChunks);
+      const size_t o = size_t(min(tile * C::kBT + row, p.nq - 1)) * G::kRowBytes + ch * 16;
+      dma16(Y1 + o, wbase + i * C::kThreads);
+      dma16(Y2 + o, wbase + i * C::kThreads + C::kTileChunks);
+    }
+  };
+  // Per-row constants of a query tile (see the header comment), written by
+  // the first 64 threads into the stage's constant arrays.
+  auto cwrite = [&](int tile, int stage) {
+    if (tid < C::kBT) {
+      const int row = tile * C::kBT + tid;
+      float *cst = cstage[stage];
+      if (row < p.nq) {
+        const size_t i = size_t(bh) * p.nq + row;
+        const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
+        cst[tid] = -lse1 * p.inv_scale;
+        cst[C::kBT + tid] = (kl - lse2) * p.inv_scale;
+        cst[2 * C::kBT + tid] = p.dkl ? p.dkl[i] : 1.f;
+        cst[3 * C::kBT + tid] = -kl * p.inv_scale * p.c;
+      } else {  // rows past N_Q: P = 0 and s1' - s2'' = 0
+        cst[tid] = -1e30f;
+        cst[C::kBT + tid] = -1e30f;
+        cst[2 * C::kBT + tid] = 0.f;
+        cst[3 * C::kBT + tid] = 0.f;
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(tile0, 0);
+    cwrite(tile0, 0);
+  }
+  __syncthreads();  // the stationary tiles, the first query tile and its constants
+
+  // K_t fragments of the dQ products (B operand: lane = column of d, 8 keys
+  // per half), read once from the stationary tiles with transposing reads.
+  // Key order within a 16-key step: position 4t + j holds key
+  // 16 ks + 8 t + 4 h + j, the order the e buffer reads below use as well.
+  const int mb = wave % kMB;
+  const int kg = wave / kMB;
+  // Key fragments of the score products (B operand: lane = key, the chunks
+  // of its half of d).  A key past N_K reads the repeated last row; its
+  // scores are masked.
+  u32x4 xf1[G::kLaneChunks], xf2[G::kLaneChunks];
+  {
+    const int xrow = wave * 32 + col;
+#pragma unroll
+    for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+      const int pos = xrow * G::kChunks + swz<G::kChunks>(xrow, frag_chunk<true, D>(h, cc));
+      xf1[cc] = xtile[pos];
+      xf2[cc] = xtile[C::kXChunks + pos];
+    }
+  }
+  u32x4 kt1[C::kKSteps], kt2[C::kKSteps];
+  {
+    const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+        const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
+        if (kG1) {
+          const u32x2 v = read_tr(reinterpret_cast<const char *>(xtile) + byte);
+          kt1[ks][2 * t] = v[0];
+          kt1[ks][2 * t + 1] = v[1];
+        }
+        if (kG2) {
+          const u32x2 v = read_tr(reinterpret_cast<const char *>(xtile + C::kXChunks) + byte);
+          kt2[ks][2 * t] = v[0];
+          kt2[ks][2 * t + 1] = v[1];
+        }
+      }
+    }
+  }
+  __syncthreads();  // everyone has its fragments: the space is free for stage 1 and the e buffers
+
+  f32x16 acc1[kMB], acc2[kMB];
+#pragma unroll
+  for (int m = 0; m < kMB; ++m) {
+    acc1[m] = f32x16{};
+    acc2[m] = f32x16{};
+  }
+  const float c = p.c;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int tile = tile0 + it;
+    const int stage = it & 1;
+    if (it + 1 < ntiles) issue(tile + 1, stage ^ 1);
+    const u32x4 *ybase = stage ? ystage1 : ystage0;
+    const float *cst = cstage[stage];
+
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      const int tb = tile * C::kBT + sb * 32;
+      if (tb >= p.nq) continue;  // the whole block is past N_Q: no e values, no dQ rows
+      // 1. scores of the wave's 32 keys against the block's 32 queries,
+      //    starting from the queries' row constants; inadmissible pairs
+      //    (causal frontier, rows past N_Q, keys past N_K) start at -1e30.
+      f32x16 s1, s2;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = sb * 32 + g4 * 8 + 4 * h;
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(cst + r0);
+        const f32x4 v2 = *reinterpret_cast<const f32x4 *>(cst + C::kBT + r0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s1[4 * g4 + q] = v1[q];
+          s2[4 * g4 + q] = v2[q];
+        }
+      }
+      const bool straddles = keys_past_end || tb + 31 > p.nq - 1 || (CAUSAL && tb < max(w0 + 31 - off, 0));
+      if (straddles) {
+        const int rel = tb + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = rel + c_row(r, 0);
+          const bool ok = srow < p.nk && t >= lim && t < p.nq;
+          s1[r] = ok ? s1[r] : -1e30f;
+          s2[r] = ok ? s2[r] : -1e30f;
+        }
+      }
+      {
+        const int arow = sb * 32 + col;
+#pragma unroll
+        for (int cc = 0; cc < G::kLaneChunks; ++cc) {
+          const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<true, D>(h, cc));
+          mfma_chunk<true>(ybase[pos], xf1[cc], s1);
+          mfma_chunk<true>(ybase[C::kTileChunks + pos], xf2[cc], s2);
+        }
+      }
+      // 2. e1, e2 packed to bf16: pk[ks][w] holds rows c_row(8ks + 2w, h)
+      //    and c_row(8ks + 2w + 1, h).
+      u32x4 pk1[2], pk2[2];
+      {
+        float e1[16], e2[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = sb * 32 + g4 * 8 + 4 * h;
+          const f32x4 KCv = *reinterpret_cast<const f32x4 *>(cst + 3 * C::kBT + r0);
+          f32x4 Gv;
+          if (GSIGN) Gv = *reinterpret_cast<const f32x4 *>(cst + 2 * C::kBT + r0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * g4 + q;
+            const float p1 = fast_exp2(s1[r] * c);
+            const float p2 = kG2 ? fast_exp2(fmaf(s2[r], c, KCv[q])) : 0.f;
+            if (GSIGN) {
+              const float gp1 = p1 * Gv[q];
+              e2[r] = fmaf(p2, Gv[q], -gp1);
+              e1[r] = gp1 * (s1[r] - s2[r]);
+            } else {
+              e2[r] = p2 - p1;
+              e1[r] = p1 * (s1[r] - s2[r]);
+            }
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pk1[ks][w] = pack_bf16(e1[8 * ks + 2 * w], e1[8 * ks + 2 * w + 1]);
+            pk2[ks][w] = pack_bf16(e2[8 * ks + 2 * w], e2[8 * ks + 2 * w + 1]);
+          }
+      }
+      // 3. dK_t^T += Q_t^T e_t: Q_t^T from transposing reads of the tile
+      //    (lane (s, grp) supplies query row sb*32 + 16ks + 8t + 4h + s/4,
+      //    columns m*32 + 16(grp&1) + 4(s&3) .. +3).
+      auto grad = [&](const char *yb, const u32x4 (&pk)[2], f32x16 (&acc)[kMB]) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int m = 0; m < kMB; ++m) {
+            const int d0 = m * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+            u32x4 a;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+              const u32x2 v = read_tr(yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2);
+              a[2 * t] = v[0];
+              a[2 * t + 1] = v[1];
+            }
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, pk[ks]), acc[m], 0, 0, 0);
+          }
+      };
+      if (kG1) grad(reinterpret_cast<const char *>(ybase), pk1, acc1);
+      if (kG2) grad(reinterpret_cast<const char *>(ybase + C::kTileChunks), pk2, acc2);
+      // 4. e_t -> the e buffer, row = the lane's key (within the workgroup),
+      //    4 consecutive queries (32 sb + 8 g4 + 4 h ..) per store.
+      {
+        const int key = wave * 32 + col;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q = sb * 32 + 8 * g4 + 4 * h;
+          const int ks = g4 >> 1, w = 2 * (g4 & 1);
+          if (kG1) *reinterpret_cast<u32x2 *>(ebuf + ebyte(key, q)) = u32x2{pk1[ks][w], pk1[ks][w + 1]};
+          if (kG2) *reinterpret_cast<u32x2 *>(ebuf + C::kEBytes + ebyte(key, q)) = u32x2{pk2[ks][w], pk2[ks][w + 1]};
+        }
+      }
+    }
+    __syncthreads();  // every wave's e blocks of this tile are in the buffer
+
+    // 5. dQ_t block (32 queries x the wave's 32 columns of d) = e_t x K_t over
+    //    the wave's key group, then added to the fp32 sums with atomics.
+    //    A operand: e_t with lane = query, 8 keys per half, by transposing
+    //    reads of the [key][query] buffer (lane (s, grp) supplies key row
+    //    16ks + 8t + 4h + s/4, queries 32sb + 16(grp&1) + 4(s&3) .. +3).
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      if (tile * C::kBT + sb * 32 >= p.nq) continue;  // skipped above as well
+      const int qa = sb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+      auto dq_block = [&](const char *eb, const u32x4 (&kt)[C::kKSteps], float *ws) {
+        f32x16 a = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::kKSteps; ++ks) {
+          u32x4 e;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int key = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+            const u32x2 v = read_tr(eb + ebyte(key, qa));
+            e[2 * t] = v[0];
+            e[2 * t + 1] = v[1];
+          }
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), __builtin_bit_cast(bf16x8, kt[ks]),
+                                                      a, 0, 0, 0);
+        }
+        // a[r]: query tile*64 + 32 sb + c_row(r, h), column mb*32 + col.
+        const int qb = tile * C::kBT + sb * 32;
+        float *base = ws + (size_t(bh) * p.nq + qb) * D + mb * 32 + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = c_row(r, h);
+          if (qb + q < p.nq) unsafeAtomicAdd(base + size_t(q) * D, a[r]);
+        }
+      };
+      if (kG1) dq_block(ebuf, kt1, p.ws1);
+      if (kG2) dq_block(ebuf + C::kEBytes, kt2, p.ws2);
+    }
+
+    if (it + 1 < ntiles) cwrite(tile + 1, stage ^ 1);
+    __syncthreads();  // the next tile's copies and constants; the e buffer is free again
+  }
+
+  // dK write-out: dK1 = scale^2 acc1, dK2 = scale acc2 (g is inside e).
+  if (srow < p.nk) {
+    const size_t ro = koff + size_t(srow) * G::kRowBytes;
+    auto store = [&](char *O, float f, const f32x16 (&A)[kMB]) {
+#pragma unroll
+      for (int m = 0; m < kMB; ++m)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = m * 32 + g4 * 8 + 4 * h;
+          *reinterpret_cast<u32x2 *>(O + ro + d0 * 2) =
+              u32x2{pack_bf16(A[m][4 * g4] * f, A[m][4 * g4 + 1] * f), pack_bf16(A[m][4 * g4 + 2] * f, A[m][4 * g4 + 3] * f)};
+        }
+    };
+    if (kG1) store(p.dk1, p.scale * p.scale, acc1);
+    if (kG2) store(p.dk2, p.scale, acc2);
+  }
+}
+
+// Zeroes n4 float4 values.
+__global__ __launch_bounds__(256) void zero_kernel(f32x4 *x, size_t n4) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256) x[i] = f32x4{};
+}
+
+// dq = f * ws, fp32 -> bf16 (nearest even); 4 values per thread.
+__global__ __launch_bounds__(256) void convert_kernel(const f32x4 *ws, size_t n4, float f, u32x2 *out) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 v = ws[i];
+  out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
+}
+
+template <int D, bool CAUSAL, int MASK, bool GSIGN>
+hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
+  using C = FusedCfg<D>;
+  FusedParams p;
+  p.q1 = static_cast<const char *>(a.q1);
+  p.k1 = static_cast<const char *>(a.k1);
+  p.q2 = static_cast<const char *>(a.q2);
+  p.k2 = static_cast<const char *>(a.k2);
+  p.kl = a.kl;
+  p.lse1 = a.lse1;
+  p.lse2 = a.lse2;
+  p.dkl = a.dkl;
+  p.dk1 = static_cast<char *>(a.dk1);
+  p.dk2 = static_cast<char *>(a.dk2);
+  const size_t n = size_t(a.bh) * a.nq * D;  // values per requested gradient
+  p.ws1 = ws;
+  p.ws2 = ws + ((MASK & 1) ? n : 0);
+  p.nq = a.nq;
+  p.nk = a.nk;
+  p.nsb = (a.nk + C::kBS - 1) / C::kBS;
+  p.scale = a.scale;
+  p.c = float(double(a.scale) * 1.4426950408889634);
+  p.inv_scale = float(1.0 / double(a.scale));
+  const int ngrad = ((MASK & 1) ? 1 : 0) + ((MASK & 2) ? 1 : 0);
+  const size_t n4 = n / 4;  // D is a multiple of 4
+  if (n4 > 0) {
+    const size_t zb = std::min<size_t>((n4 * ngrad + 255) / 256, 4096);
+    zero_kernel<<<dim3(unsigned(zb)), dim3(256), 0, stream>>>(reinterpret_cast<f32x4 *>(ws), n4 * ngrad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long blocks = (long long)p.nsb * a.bh;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  if (blocks > 0) {
+    const void *fn = reinterpret_cast<const void *>(&fused_bwd_kernel<D, CAUSAL, MASK, GSIGN>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (e != hipSuccess) return e;
+    void *args[] = {&p};
+    e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (n4 > 0) {
+    const size_t cb = (n4 + 255) / 256;
+    if (cb > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
+    if (MASK & 1)
+      convert_kernel<<<dim3(unsigned(cb)), dim3(256), 0, stream>>>(reinterpret_cast<const f32x4 *>(p.ws1), n4,
+                                                                   a.scale * a.scale, static_cast<u32x2 *>(a.dq1));
+    if (MASK & 2)
+      convert_kernel<<<dim3(unsigned(cb)), dim3(256), 0, stream>>>(reinterpret_cast<const f32x4 *>(p.ws2), n4,
+                                                                   a.scale, static_cast<u32x2 *>(a.dq2));
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fused_masks(const BwdArgs &a, float *ws, hipStream_t s) {
+  const bool gsign = a.dkl != nullptr;
+  switch (a.grad_mask) {
+    case 1: return gsign ? launch_fused_t<D, CAUSAL, 1, true>(a, ws, s) : launch_fused_t<D, CAUSAL, 1, false>(a, ws, s);
+    case 2: return gsign ? launch_fused_t<D, CAUSAL, 2, true>(a, ws, s) : launch_fused_t<D, CAUSAL, 2, false>(a, ws, s);
+    default: return gsign ? launch_fused_t<D, CAUSAL, 3, true>(a, ws, s) : launch_fused_t<D, CAUSAL, 3, false>(a, ws, s);
+  }
+}
+
+}  // namespace
+
+size_t bwd_fused_workspace_floats(int bh, int nq, int d, int grad_mask) {
+  if (bh <= 0 || nq <= 0) return 0;
+  const int ngrad = ((grad_mask & 1) ? 1 : 0) + ((grad_mask & 2) ? 1 : 0);
+  return size_t(bh) * size_t(nq) * size_t(d) * size_t(ngrad);
+}
+
+hipError_t launch_bwd_fused(const BwdArgs &a, float *ws, hipStream_t stream) {
+  if (!a.bf16) return hipErrorInvalidValue;
+  if (a.d == 64) return a.causal ? launch_fused_masks<64, true>(a, ws, stream) : launch_fused_masks<64, false>(a, ws, stream);
+  return a.causal ? launch_fused_masks<128, true>(a, ws, stream) : launch_fused_masks<128, false>(a, ws, stream);
+}
+
+}  // namespace streamkl

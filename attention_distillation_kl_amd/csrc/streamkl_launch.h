@@ -39,5 +39,10 @@ int bwd_dq_default_splits(int bh, int nq, int nk, int d, bool bf16, int grad_mas
 size_t bwd_dq_workspace_floats(int bh, int nq, int d, int grad_mask, int splits);
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
+// The single-pass backward (bf16 only): dK in registers, dQ added with
+// atomics into `ws` (fp32, bwd_fused_workspace_floats values: the query
+// gradients asked for, one after the other), then converted into dq1 / dq2.
+size_t bwd_fused_workspace_floats(int bh, int nq, int d, int grad_mask);
+hipError_t launch_bwd_fused(const BwdArgs &a, float *ws, hipStream_t stream);
 
 }  // namespace streamkl

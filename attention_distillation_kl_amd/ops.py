@@ -105,6 +105,40 @@ def streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, causal=Fa
     return dq1, dk1, dq2, dk2
 
 
+def streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, causal=False,
+                       grad_mask=_lib.GRAD_ALL, workspace=None):
+    """The single-pass backward (bf16 only): (dq1, dk1, dq2, dk2) as
+    streamkl_bwd returns them.  ``workspace``: a device tensor of at least
+    streamkl_bwd_fused_workspace_size bytes (the fp32 query-gradient sums);
+    allocated here when None."""
+    B, H, NQ, NK, d = _check_inputs(q1, k1, q2, k2)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dev = q1.device
+    for name, t in (("kl", kl), ("lse1", lse1), ("lse2", lse2)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, NQ) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, N_Q] tensor on {dev}")
+    if dkl is not None:
+        dkl = dkl.to(device=dev, dtype=torch.float32).expand(B, H, NQ).contiguous()
+    g1, g2 = bool(grad_mask & 1), bool(grad_mask & 2)
+    dq1 = torch.empty_like(q1) if g1 else None
+    dk1 = torch.empty_like(k1) if g1 else None
+    dq2 = torch.empty_like(q2) if g2 else None
+    dk2 = torch.empty_like(k2) if g2 else None
+    dt = _dtype_code(q1)
+    need = _lib.bwd_fused_workspace_size(B, H, NQ, NK, d, int(bool(causal)), dt, grad_mask)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    st = _lib.bwd_fused(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1), _ptr(lse2), _ptr(dkl),
+                        B, H, NQ, NK, d, scale, int(bool(causal)), dt, int(grad_mask),
+                        _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != _lib.OK:
+        raise _lib.StreamKLError(st, "streamkl_bwd_fused")
+    return dq1, dk1, dq2, dk2
+
+
 def streamkl_bwd_workspace(q1, k1, causal=False, grad_mask=_lib.GRAD_ALL):
     """The backward's workspace for these sizes (a uint8 device tensor), or
     None where the library needs none (query-gradient grids that fill the GPU)."""

@@ -180,7 +180,10 @@ streamkl_status streamkl_fwd_splitk_noalloc(const void *q1, const void *k1,
  * (query block, partition) workgroup stores its fp32 partial dq_t and a
  * second kernel adds the partitions in a fixed order (deterministic, no
  * atomics); the workspace then holds splits * B*H*N_Q*d floats per requested
- * gradient, splits being the library's choice for these sizes.
+ * gradient, splits being the library's choice for these sizes.  Where
+ * streamkl_bwd_fused_selected is 1 it is the larger of that and
+ * streamkl_bwd_fused_workspace_size, so one workspace serves streamkl_bwd
+ * and streamkl_bwd_dq_ws alike.
  */
 size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
                                    int causal, int dtype, int grad_mask);
@@ -202,6 +205,10 @@ size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
  *        bytes, 16-byte aligned (may be NULL when that is 0), owned by the
  *        caller; its contents are dead once the call's work has completed.
  * With N_Q == 0 the key gradients are written as zeros.
+ * Form: where streamkl_bwd_fused_selected(...) is 1 (bf16, short query
+ * blocks, query-gradient buffer within L2) this is streamkl_bwd_fused;
+ * otherwise the two-kernel form, streamkl_bwd_dk then streamkl_bwd_dq_ws,
+ * whose results are bitwise reproducible.
  */
 streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
                              const void *k2, const float *kl,
@@ -227,9 +234,10 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
  * 16-byte aligned, caller-owned, STREAMKL_ERR_WORKSPACE otherwise).  Where
  * that size is not zero (short query blocks) the query gradients are
  * computed by key partitions, partial sums in the workspace, added in a
- * fixed order; otherwise it is streamkl_bwd_dq.  streamkl_bwd is
- * streamkl_bwd_dk followed by streamkl_bwd_dq_ws on one stream, with
- * bitwise the same results.
+ * fixed order; otherwise it is streamkl_bwd_dq.  Where the fused form is
+ * not selected, streamkl_bwd is streamkl_bwd_dk followed by
+ * streamkl_bwd_dq_ws on one stream, with bitwise the same results; where it
+ * is, the two halves remain a deterministic alternative to it.
  */
 streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2,
                                 const void *k2, const float *kl,
@@ -253,6 +261,54 @@ streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2,
                                 int N_K, int d, float scale, int causal,
                                 int dtype, int grad_mask, void *dk1, void *dk2,
                                 void *stream);
+
+/*
+ * streamkl_bwd_fused_workspace_size -- bytes of device workspace
+ * streamkl_bwd_fused needs: one fp32 [B, H, N_Q, d] array per requested query
+ * gradient (the sums its atomics add into).  0 for STREAMKL_F32 (not
+ * supported by the fused form), for invalid sizes and for N_Q == 0.
+ */
+size_t streamkl_bwd_fused_workspace_size(int B, int H, int N_Q, int N_K,
+                                         int d, int causal, int dtype,
+                                         int grad_mask);
+
+/*
+ * streamkl_bwd_fused_selected -- 1 where streamkl_bwd runs the fused form:
+ * the page's criterion (the query-gradient buffer, one fp32 [B, H, N_Q, d]
+ * array per requested gradient, fits in the 32 MiB of L2 of the eight XCDs),
+ * bf16 inputs, and short query blocks where it measured faster than the
+ * two-kernel form: 1 <= N_Q <= 64 at d = 128 (one query tile per head),
+ * 1 <= N_Q <= 8 at d = 64; 0 otherwise.
+ */
+int streamkl_bwd_fused_selected(int B, int H, int N_Q, int N_K, int d,
+                                int causal, int dtype, int grad_mask);
+
+/*
+ * streamkl_bwd_fused -- the single-pass recompute backward ("Strategia di
+ * Ricalcolo", kernel-fusion bullet: each (query tile, key tile) pair is
+ * visited once, key gradients are kept in registers and query gradients are
+ * added with atomics into a buffer; the page's ablation bullet of
+ * "Risultati Sperimentali" finds it faster for short query blocks).
+ * Same arguments, meaning and results as streamkl_bwd, for bf16 inputs only:
+ *   workspace / workspace_bytes: at least streamkl_bwd_fused_workspace_size
+ *        bytes, 16-byte aligned, owned by the caller; cleared and written by
+ *        the call, dead once its work has completed on `stream`.
+ * Each pair's recompute is done once (12 d flops per admissible pair instead
+ * of the two-kernel form's 16).  The fp32 additions of the query gradients
+ * happen in a varying order, so dq1 / dq2 can differ in the last bits from
+ * run to run; dk1 / dk2 are bitwise reproducible.
+ * Errors as streamkl_bwd, plus STREAMKL_ERR_UNSUPPORTED for STREAMKL_F32 and
+ * STREAMKL_ERR_WORKSPACE for a missing, misaligned or short workspace.
+ */
+streamkl_status streamkl_bwd_fused(const void *q1, const void *k1,
+                                   const void *q2, const void *k2,
+                                   const float *kl, const float *lse1,
+                                   const float *lse2, const float *dkl, int B,
+                                   int H, int N_Q, int N_K, int d, float scale,
+                                   int causal, int dtype, int grad_mask,
+                                   void *dq1, void *dk1, void *dq2, void *dk2,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *streamkl_status_str(int status);

@@ -62,8 +62,13 @@ def fwd(**kw):
 def bwd(**kw):
     a = dict(q1=A, k1=A2, q2=A3, k2=A4, kl=O1, lse1=O2, lse2=O3, dkl=None, B=1, H=2, NQ=64, NK=64,
              d=128, scale=0.125, causal=1, dtype=_lib.BF16, mask=3, dq1=0x80000, dk1=0x90000,
-             dq2=0xA0000, dk2=0xB0000, ws=None, wsb=0, stream=None)
+             dq2=0xA0000, dk2=0xB0000, ws=None, wsb=None, stream=None)
     a.update(kw)
+    if a["wsb"] is None:  # the declared workspace, at a fake address when there is one
+        a["wsb"] = _lib.bwd_workspace_size(a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["causal"], a["dtype"],
+                                           a["mask"])
+        if a["wsb"] and a["ws"] is None:
+            a["ws"] = 0xC0000
     return _lib.bwd(a["q1"], a["k1"], a["q2"], a["k2"], a["kl"], a["lse1"], a["lse2"], a["dkl"],
                     a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["scale"], a["causal"], a["dtype"],
                     a["mask"], a["dq1"], a["dk1"], a["dq2"], a["dk2"], a["ws"], a["wsb"], a["stream"])
@@ -187,18 +192,74 @@ def test_backward_workspace_query(lib):
         assert _lib.bwd_workspace_size(2, 32, 8192, 8192, 128, 1, _lib.BF16, mask) == 0
     # short query blocks: key partitions, splits * B*H*N_Q*d floats per requested gradient
     for mask, ngrad in ((1, 1), (2, 1), (3, 2)):
-        ws = _lib.bwd_workspace_size(1, 4, 64, 8192, 128, 1, _lib.BF16, mask)
-        assert ws > 0 and ws % (4 * 64 * 128 * 4 * ngrad) == 0
-        splits = ws // (4 * 64 * 128 * 4 * ngrad)
+        ws = _lib.bwd_workspace_size(1, 4, 100, 8192, 128, 1, _lib.BF16, mask)
+        assert ws > 0 and ws % (4 * 100 * 128 * 4 * ngrad) == 0
+        splits = ws // (4 * 100 * 128 * 4 * ngrad)
         assert 2 <= splits <= 256 and (8192 // 64) >= 4 * splits
-    assert _lib.bwd_workspace_size(1, 4, 64, 128, 128, 1, _lib.BF16, 3) == 0   # too few key tiles
-    assert _lib.bwd_workspace_size(1, 4, 64, 8192, 96, 1, _lib.BF16, 3) == 0   # invalid sizes
+    assert _lib.bwd_workspace_size(1, 4, 100, 128, 128, 1, _lib.BF16, 3) == 0   # too few key tiles
+    assert _lib.bwd_workspace_size(1, 4, 64, 8192, 96, 1, _lib.BF16, 3) == 0    # invalid sizes
+
+
+def test_fused_backward_selection_and_workspace(lib):
+    """streamkl_bwd takes the fused form for bf16 with at most 64 queries per
+    head at d = 128 (8 at d = 64) while the fp32 query-gradient buffer fits
+    the 32 MiB of L2; its workspace is then at least one [B, H, N_Q, d] fp32
+    array per requested gradient (and still at least what the partitioned
+    query half needs)."""
+    sel = _lib.bwd_fused_selected
+    for nq in (1, 17, 64):
+        assert sel(1, 32, nq, 65536, 128, 1, _lib.BF16, 3) == 1
+    for nq in (1, 8):
+        assert sel(1, 32, nq, 65536, 64, 0, _lib.BF16, 1) == 1
+    assert sel(1, 32, 9, 65536, 64, 0, _lib.BF16, 1) == 0
+    assert sel(1, 32, 65, 65536, 128, 1, _lib.BF16, 3) == 0       # a second query tile
+    assert sel(1, 32, 64, 65536, 128, 1, _lib.F32, 3) == 0        # bf16 only
+    assert sel(1, 32, 0, 65536, 128, 1, _lib.BF16, 3) == 0        # nothing to add
+    # 1024 heads of 64 queries: 64 MiB of fp32 sums for both gradients, 32 MiB for one
+    assert sel(1, 1024, 64, 4096, 128, 0, _lib.BF16, 3) == 0
+    assert sel(1, 1024, 64, 4096, 128, 0, _lib.BF16, 1) == 1
+    assert sel(1, 1025, 64, 4096, 128, 0, _lib.BF16, 1) == 0
+    assert sel(1, 2, 64, 32, 128, 1, _lib.BF16, 3) == 0           # causal with more queries than keys
+    for mask, ngrad in ((1, 1), (2, 1), (3, 2)):
+        fused = _lib.bwd_fused_workspace_size(1, 4, 64, 8192, 128, 1, _lib.BF16, mask)
+        assert fused == 4 * 64 * 128 * 4 * ngrad
+        assert _lib.bwd_workspace_size(1, 4, 64, 8192, 128, 1, _lib.BF16, mask) >= fused
+    assert _lib.bwd_workspace_size(1, 4, 64, 128, 128, 1, _lib.BF16, 3) == 4 * 64 * 128 * 4 * 2
+    assert _lib.bwd_fused_workspace_size(1, 4, 64, 8192, 128, 1, _lib.F32, 3) == 0
+
+
+def test_fused_backward_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(q1=A, k1=A2, q2=A3, k2=A4, kl=O1, lse1=O2, lse2=O3, dkl=None, B=1, H=2, NQ=64, NK=8192,
+                 d=128, scale=0.125, causal=1, dtype=_lib.BF16, mask=3, dq1=0x80000, dk1=0x90000,
+                 dq2=0xA0000, dk2=0xB0000, ws=0xC0000, wsb=None, stream=None)
+        a.update(kw)
+        if a["wsb"] is None:
+            a["wsb"] = _lib.bwd_fused_workspace_size(a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["causal"],
+                                                     a["dtype"], a["mask"])
+        return _lib.bwd_fused(a["q1"], a["k1"], a["q2"], a["k2"], a["kl"], a["lse1"], a["lse2"], a["dkl"],
+                              a["B"], a["H"], a["NQ"], a["NK"], a["d"], a["scale"], a["causal"], a["dtype"],
+                              a["mask"], a["dq1"], a["dk1"], a["dq2"], a["dk2"], a["ws"], a["wsb"], a["stream"])
+    assert call(dtype=_lib.F32, wsb=1 << 20) == UNS
+    assert call(ws=None, wsb=0) == _lib.ERR_WORKSPACE
+    assert call(wsb=16) == _lib.ERR_WORKSPACE
+    assert call(ws=0xC0004) == _lib.ERR_WORKSPACE
+    assert call(d=96) == UNS
+    assert call(mask=0) == INV
+    assert call(dq1=None) == INV
+    assert call(NQ=65, NK=64) == INV
+    assert call(B=0) == _lib.OK
 
 
 def test_bwd_rejects_short_or_misaligned_workspace(lib):
-    need = _lib.bwd_workspace_size(1, 2, 64, 8192, 128, 1, _lib.BF16, 3)
-    assert need > 0
-    kw = dict(NQ=64, NK=8192)
+    for nq in (64, 100):   # the fused and the partitioned form
+        need = _lib.bwd_workspace_size(1, 2, nq, 8192, 128, 1, _lib.BF16, 3)
+        assert need > 0
+        kw = dict(NQ=nq, NK=8192)
+        assert bwd(ws=None, wsb=0, **kw) == _lib.ERR_WORKSPACE
+        assert bwd(ws=0xC0004, wsb=need, **kw) == _lib.ERR_WORKSPACE
+    need = _lib.bwd_workspace_size(1, 2, 100, 8192, 128, 1, _lib.BF16, 3)
+    kw = dict(NQ=100, NK=8192)
     assert bwd(ws=None, wsb=0, **kw) == _lib.ERR_WORKSPACE
     assert bwd(ws=0xC0000, wsb=need - 16, **kw) == _lib.ERR_WORKSPACE
     assert bwd(ws=0xC0004, wsb=need, **kw) == _lib.ERR_WORKSPACE

@@ -1,0 +1,122 @@
+"""GPU parity of the single-pass backward (streamkl_bwd_fused: dK in
+registers, dQ added with fp32 atomics) against the fp64 oracle, through the
+C ABI."""
+import math
+
+import pytest
+import torch
+
+from attention_distillation_kl_amd import _lib, make_inputs, ops
+from attention_distillation_kl_amd.inputs import upstream_grad
+from parity_util import check_grad, log, oracle_heads, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+NAMES = ("dq1", "dk1", "dq2", "dk2")
+
+
+def compare(q1, k1, q2, k2, scale, causal, g=None, mask=3, tag=""):
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    grads = dict(zip(NAMES, ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)))
+    torch.cuda.synchronize()
+    B, H = q1.shape[:2]
+    ref = oracle_heads(q1, k1, q2, k2, scale, causal, range(B * H), g=g, grads=True)
+    keep = {1: ("dq1", "dk1"), 2: ("dq2", "dk2"), 3: NAMES}[mask]
+    for hh in range(B * H):
+        b, h = divmod(hh, H)
+        for n in NAMES:
+            if n in keep:
+                check_grad(to64(grads[n][b, h]), ref[hh][n], q1.dtype, f"{tag} head {hh} {n}")
+            else:
+                assert grads[n] is None
+    return grads
+
+
+SHAPES = [
+    # B, H, NQ, NK, d, causal
+    (1, 1, 1, 1, 128, False),
+    (1, 1, 1, 1, 64, True),
+    (1, 2, 5, 300, 128, True),
+    (1, 2, 17, 63, 64, False),
+    (2, 1, 64, 1000, 128, True),
+    (1, 3, 64, 129, 128, False),
+    (1, 2, 65, 4096, 64, True),
+    (1, 1, 100, 100, 128, True),
+    (1, 2, 257, 300, 128, False),
+    (1, 1, 300, 333, 64, True),
+    (1, 2, 512, 2048, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fused_backward_matches_oracle(shape):
+    B, H, NQ, NK, d, causal = shape
+    log(f"fused bwd {shape}")
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.4, seed=NQ * 5 + NK, device=DEV)
+    compare(q1, k1, q2, k2, 1.0 / math.sqrt(d), causal, tag=str(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_backward_upstream_gradient(causal, d):
+    log(f"fused bwd upstream g d={d} causal={causal}")
+    q1, k1, q2, k2 = make_inputs(1, 2, 150, 700, d, torch.bfloat16, "student", 0.4, seed=21, device=DEV)
+    g = upstream_grad(1, 2, 150, seed=21, device=DEV)
+    compare(q1, k1, q2, k2, 0.1, causal, g=g, tag="upstream")
+
+
+@pytest.mark.parametrize("mask", [1, 2])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_backward_single_configuration(mask, d):
+    """grad_mask 1 / 2: only that configuration's tensors, and its key
+    gradients bit for bit those of the full fused backward (dK does not go
+    through atomics)."""
+    q1, k1, q2, k2 = make_inputs(1, 2, 96, 500, d, torch.bfloat16, "student", 0.3, seed=22, device=DEV)
+    part = compare(q1, k1, q2, k2, 0.09, True, mask=mask, tag=f"mask {mask}")
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 0.09, True)
+    full = dict(zip(NAMES, ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, 0.09, True)))
+    torch.cuda.synchronize()
+    n = "dk1" if mask == 1 else "dk2"
+    assert torch.equal(part[n], full[n])
+
+
+def test_fused_backward_short_query_block_over_64k_keys():
+    """The shape the fused form is for: 64 causal queries over 65536 keys,
+    32 heads; the oracle checks the first and last head."""
+    B, H, NQ, NK, d = 1, 32, 64, 65536, 128
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.2, seed=23, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, True)
+    grads = dict(zip(NAMES, ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, scale, True)))
+    torch.cuda.synchronize()
+    ref = oracle_heads(q1, k1, q2, k2, scale, True, (0, H - 1), grads=True)
+    for hh in (0, H - 1):
+        for n in NAMES:
+            check_grad(to64(grads[n][0, hh]), ref[hh][n], q1.dtype, f"64x64K head {hh} {n}")
+
+
+def test_fused_backward_identical_teacher_student_gives_zero_gradients():
+    q, k, _, _ = make_inputs(1, 2, 70, 300, 128, torch.bfloat16, "iid", 0, seed=24, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q, k, q, k, 0.1, True)
+    grads = ops.streamkl_bwd_fused(q, k, q, k, kl, l1, l2, None, 0.1, True)
+    torch.cuda.synchronize()
+    for n, t in zip(NAMES, grads):
+        assert torch.count_nonzero(t) == 0, n
+
+
+def test_fused_backward_no_queries_gives_zero_key_gradients():
+    q1, k1, q2, k2 = make_inputs(1, 2, 0, 70, 128, torch.bfloat16, "iid", 0, seed=25, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 0.1, False)
+    _, dk1, _, dk2 = ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, 0.1, False)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk1) == 0 and torch.count_nonzero(dk2) == 0
+
+
+def test_fused_backward_key_gradients_are_deterministic():
+    q1, k1, q2, k2 = make_inputs(1, 4, 200, 3000, 128, torch.bfloat16, "student", 0.2, seed=26, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 0.09, True)
+    a = ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, 0.09, True)
+    b = ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, 0.09, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[3], b[3])

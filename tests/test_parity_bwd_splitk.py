@@ -18,9 +18,23 @@ NAMES = ("dq1", "dk1", "dq2", "dk2")
 
 
 def partitions_used(q1, k1, causal, mask):
+    """Whether the query half takes key partitions: its workspace (which
+    streamkl_bwd_workspace_size covers) exceeds what the fused form needs."""
     B, H, NQ, d = q1.shape
     dt = _lib.BF16 if q1.dtype == torch.bfloat16 else _lib.F32
-    return _lib.bwd_workspace_size(B, H, NQ, k1.shape[2], d, int(causal), dt, mask) > 0
+    ws = _lib.bwd_workspace_size(B, H, NQ, k1.shape[2], d, int(causal), dt, mask)
+    if _lib.bwd_fused_selected(B, H, NQ, k1.shape[2], d, int(causal), dt, mask):
+        return ws > _lib.bwd_fused_workspace_size(B, H, NQ, k1.shape[2], d, int(causal), dt, mask)
+    return ws > 0
+
+
+def two_kernel_backward(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask):
+    """streamkl_bwd_dk, then streamkl_bwd_dq_ws with the backward's
+    workspace: the two-kernel form, whichever form streamkl_bwd picks."""
+    ws = ops.streamkl_bwd_workspace(q1, k1, causal, mask)
+    dk = ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
+    dq = ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask, workspace=ws)
+    return dq[0], dk[0], dq[1], dk[1]
 
 
 # B, H, NQ, NK, d, dtype, causal, mask
@@ -44,7 +58,7 @@ def test_partitioned_query_gradients_match_oracle(case):
     scale = d ** -0.5
     g = upstream_grad(B, H, NQ, seed=NQ, device=DEV)
     kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
-    grads = dict(zip(NAMES, ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)))
+    grads = dict(zip(NAMES, two_kernel_backward(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)))
     torch.cuda.synchronize()
     ref = oracle_heads(q1, k1, q2, k2, scale, causal, range(B * H), g=g, grads=True)
     want = [n for n in NAMES if (mask & 1 and n.endswith("1")) or (mask & 2 and n.endswith("2"))]
@@ -72,39 +86,59 @@ def test_partitioned_query_gradients_are_deterministic_and_agree_with_one_partit
         assert rel < 4e-3, rel  # bf16 rounding of two fp32 summation orders
 
 
-# B, H, NQ, NK, d, causal, mask, partitioned
+# B, H, NQ, NK, d, causal, mask, partitioned, fused (the form streamkl_bwd picks)
 HALF_CASES = [
-    (1, 4, 128, 8192, 128, True, 3, True),
-    (1, 2, 70, 3000, 64, True, 1, True),
-    (1, 3, 1, 8192, 64, False, 3, True),      # decoding row
-    (1, 2, 70, 3000, 128, False, 2, True),
-    (2, 2, 33, 5000, 64, True, 1, True),
-    (1, 32, 2048, 2048, 128, True, 3, False),
+    (1, 4, 128, 8192, 128, True, 3, True, False),
+    (1, 2, 70, 3000, 64, True, 1, True, False),
+    (1, 3, 1, 8192, 64, False, 3, True, True),      # decoding row
+    (1, 2, 70, 3000, 128, False, 2, True, False),
+    (2, 2, 33, 5000, 64, True, 1, True, False),
+    (2, 2, 33, 5000, 128, True, 1, True, True),
+    (1, 32, 2048, 2048, 128, True, 3, False, False),
 ]
 
 
 @pytest.mark.parametrize("case", HALF_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_halves_with_the_workspace_reproduce_streamkl_bwd(case):
     """streamkl_bwd_dk then streamkl_bwd_dq_ws is streamkl_bwd, bit for bit,
-    whether or not the sizes call for key partitions."""
-    B, H, NQ, NK, d, causal, mask, partitioned = case
+    whether or not the sizes call for key partitions -- where streamkl_bwd
+    keeps the two-kernel form.  Where it takes the fused form, it is
+    streamkl_bwd_fused: the same key gradients bit for bit, query gradients
+    equal up to the order of the atomic fp32 additions; the halves agree
+    with it to bf16 rounding."""
+    B, H, NQ, NK, d, causal, mask, partitioned, fused = case
     log(f"bwd halves with workspace {case}")
     q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=NQ + 7, device=DEV)
     scale = d ** -0.5
     g = upstream_grad(B, H, NQ, seed=11, device=DEV)
+    assert _lib.bwd_fused_selected(B, H, NQ, NK, d, int(causal), _lib.BF16, mask) == int(fused)
+    assert partitions_used(q1, k1, causal, mask) == partitioned
     kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, scale, causal)
     full = ops.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
     ws = ops.streamkl_bwd_workspace(q1, k1, causal, mask)
-    assert (ws is not None) == partitioned
+    assert (ws is not None) == (partitioned or fused)
     if ws is None:  # the entry point with an empty workspace, which these sizes allow
         ws = torch.empty(0, device=DEV, dtype=torch.uint8)
     dk = ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
     dq = ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask, workspace=ws)
+    halves = (dq[0], dk[0], dq[1], dk[1])
+    if fused:
+        direct = ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, mask)
     torch.cuda.synchronize()
-    for got, want in zip((dq[0], dk[0], dq[1], dk[1]), full):
+    for i, (got, want) in enumerate(zip(halves, full)):
         assert (got is None) == (want is None)
-        if want is not None:
+        if want is None:
+            continue
+        if not fused:
             assert torch.equal(got, want)
+            continue
+        if i % 2 == 1:   # key gradients: no atomics
+            assert torch.equal(direct[i], want)
+        else:
+            rel = ((direct[i].double() - want.double()).norm() / want.double().norm().clamp_min(1e-30)).item()
+            assert rel < 4e-3, rel
+        rel = ((got.double() - want.double()).norm() / want.double().norm().clamp_min(1e-30)).item()
+        assert rel < 4e-3, rel
     if partitioned:  # a workspace one granule short is refused before anything is enqueued
         short = ws[: ws.numel() - 16]
         with pytest.raises(_lib.StreamKLError, match="STREAMKL_ERR_WORKSPACE"):
