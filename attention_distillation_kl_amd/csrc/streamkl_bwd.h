@@ -20,9 +20,9 @@
 //   ROLE_DQ: a workgroup owns 256 query rows ("stationary"; 128 for fp32
 //            with d = 128) and streams key tiles ("streamed") up to its
 //            causal frontier; it accumulates dQ.
-//   ROLE_DK: a workgroup owns 64 key rows (bf16, both gradients; else 128)
-//            and streams query tiles from its causal frontier to N_Q; it
-//            accumulates dK.
+//   ROLE_DK: a workgroup owns 256 key rows (128 for fp32 with d = 128; 64
+//            in the paired layout for small grids) and streams query tiles
+//            from its causal frontier to N_Q; it accumulates dK.
 // Both recompute S1, S2; neither needs atomics, and results are bitwise
 // deterministic.  For short query blocks the query-gradient role can also run
 // by key partitions (SPLIT below): partial sums in a caller's workspace, added
@@ -57,16 +57,20 @@ namespace streamkl {
 
 enum { ROLE_DQ = 0, ROLE_DK = 1 };
 
-// PAIR (bf16, both gradients): the two waves of a pair own the same 32
-// stationary rows.  Per streamed tile each recomputes the scores of one of the
-// two 32-row blocks and forms e1, e2 there; they swap one of the two through
-// LDS, and then wave 0 accumulates the teacher's gradient and wave 1 the
-// student's over both blocks, each starting with the block it scored.  A wave then holds one d x 32 accumulator
-// instead of two and both stationary fragments fit in registers at two waves
-// per SIMD.
-// Otherwise (one gradient, or fp32) every wave owns its own 32 stationary rows
-// and accumulates what is asked for; the teacher's stationary fragments live
-// in an LDS tile wherever two waves per SIMD need the registers.
+// PAIR (key-gradient role, bf16, both gradients, small grids): the two waves
+// of a pair own the same 32 stationary rows.  Per streamed tile each
+// recomputes the scores of one of the two 32-row blocks and forms e1, e2
+// there; they swap one of the two through LDS, and then wave 0 accumulates
+// the teacher's gradient and wave 1 the student's over both blocks, each
+// starting with the block it scored.  A wave then holds one d x 32
+// accumulator instead of two and both stationary fragments fit in registers
+// at two waves per SIMD, in workgroups of 64 keys (two per CU).
+// Otherwise every wave owns its own 32 stationary rows and accumulates what
+// is asked for; the teacher's stationary fragments live in an LDS tile
+// wherever two waves per SIMD need the registers (workgroups of 8 waves, 256
+// rows, one per CU).  For the key-gradient role this one-barrier-per-tile
+// layout is 4-10% faster on large grids with long query streams; the paired
+// one, with 4x the workgroups, wins on small grids (bwd_dk_paired below).
 template <bool BF16, int D, bool PAIR>
 struct BwdCfg {
   using G = RowGeom<BF16, D>;
@@ -137,25 +141,42 @@ __device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bo
   return r;
 }
 
-// The paired layout pays off in the key-gradient role; the query-gradient
-// role is faster with one wave per 32 stationary rows.
-template <bool BF16, int MASK, int ROLE>
-constexpr bool kPairOf = BF16 && MASK == 3 && ROLE == ROLE_DK;
+// PO ("paired order"): the key-gradient role on a grid small enough for the
+// paired layout.  With both gradients it selects that layout; with the
+// student's gradient alone it takes the streamed blocks in the order the
+// paired student wave does, so that both give the same bits.  The
+// query-gradient role always runs one wave per 32 stationary rows.
+template <bool BF16, int MASK, int ROLE, bool PO>
+constexpr bool kPairOf = PO && BF16 && MASK == 3 && ROLE == ROLE_DK;
 
-template <bool BF16, int D, int MASK, int ROLE>
-using BwdCfgOf = BwdCfg<BF16, D, kPairOf<BF16, MASK, ROLE>>;
+template <bool BF16, int D, int MASK, int ROLE, bool PO = false>
+using BwdCfgOf = BwdCfg<BF16, D, kPairOf<BF16, MASK, ROLE, PO>>;
+
+// Whether the key-gradient role takes the paired layout (bf16, both
+// gradients).  The unpaired layout -- one 256-key workgroup per CU, which
+// loads its 256 stationary keys before streaming -- needs at least two rounds
+// of workgroups and query streams of 8192 rows to pay off.  Measured (dK
+// kernel, causal, d = 128 unless stated; paired / unpaired time):
+//   H x N = 8 x 2048: 0.51;  32 x 2048: 0.86;  16 x 4096: 0.75;
+//   8 x 8192: 0.77;  32 x 4096: 0.84;  16 x 8192: 1.04;  64 x 8192: 1.04;
+//   4 x 32768: 1.08;  2 x 65536: 1.10;  32 x 8192 (d = 64): 1.09.
+inline bool bwd_dk_paired(int bh, int nq, int nk, bool bf16) {
+  if (!bf16) return false;
+  const long long unpaired = (long long)bh * ((nk + 255) / 256);
+  return unpaired < 2 * 256 || nq < 8192;
+}
 
 // SPLIT (query-gradient role only): the workgroup folds one key partition and
 // stores fp32 partial gradients instead of the gradients themselves.
-template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(BwdCfgOf<BF16, D, MASK, ROLE>::kThreads,
-                                                      BwdCfgOf<BF16, D, MASK, ROLE>::kThreads),
-                          amdgpu_waves_per_eu(BwdCfgOf<BF16, D, MASK, ROLE>::kWavesPerEU,
-                                              BwdCfgOf<BF16, D, MASK, ROLE>::kWavesPerEU)))
+template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool SPLIT, bool PO>
+__global__ __attribute__((amdgpu_flat_work_group_size(BwdCfgOf<BF16, D, MASK, ROLE, PO>::kThreads,
+                                                      BwdCfgOf<BF16, D, MASK, ROLE, PO>::kThreads),
+                          amdgpu_waves_per_eu(BwdCfgOf<BF16, D, MASK, ROLE, PO>::kWavesPerEU,
+                                              BwdCfgOf<BF16, D, MASK, ROLE, PO>::kWavesPerEU)))
 void bwd_kernel(BwdParams p) {
-  using C = BwdCfgOf<BF16, D, MASK, ROLE>;
+  using C = BwdCfgOf<BF16, D, MASK, ROLE, PO>;
   using G = typename C::G;
-  constexpr bool kPair = kPairOf<BF16, MASK, ROLE>;
+  constexpr bool kPair = kPairOf<BF16, MASK, ROLE, PO>;
   constexpr bool kG1 = (MASK & 1) != 0;
   constexpr bool kG2 = (MASK & 2) != 0;
   constexpr int kMB = D / 32;  // 32-row blocks of d in the gradient accumulators
@@ -610,10 +631,11 @@ void bwd_kernel(BwdParams p) {
       grad_bf16(hc, yb, mine, acc1);
       grad_bf16(1 - hc, yb, theirs, acc1);
     } else {
-      // The key-gradient role with the student's gradient alone takes the
-      // blocks in the order the paired kernel's student wave does (its own
-      // block, 1, first), so both give the same bits.
-      constexpr bool kRev = BF16 && ROLE == ROLE_DK && MASK == 2;
+      // The key-gradient role with the student's gradient alone, on a grid
+      // where both gradients take the paired layout, takes the blocks in the
+      // order the paired kernel's student wave does (its own block, 1,
+      // first), so both give the same bits.
+      constexpr bool kRev = PO && BF16 && ROLE == ROLE_DK && MASK == 2;
 #pragma unroll
       for (int i = 0; i < C::kSub; ++i) {
         const int sb = kRev ? C::kSub - 1 - i : i;
@@ -715,10 +737,10 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict_
   }
 }
 
-template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN>
+template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool PO>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   constexpr bool kCanSplit = ROLE == ROLE_DQ;
-  using C = BwdCfgOf<BF16, D, MASK, ROLE>;
+  using C = BwdCfgOf<BF16, D, MASK, ROLE, PO>;
   BwdParams p;
   p.q1 = static_cast<const char *>(a.q1);
   p.k1 = static_cast<const char *>(a.k1);
@@ -748,8 +770,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const long long blocks = (long long)p.nsb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-  const void *fn = split ? reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, kCanSplit>)
-                         : reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, false>);
+  const void *fn = split ? reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, kCanSplit, PO>)
+                         : reinterpret_cast<const void *>(&bwd_kernel<BF16, D, CAUSAL, ROLE, MASK, GSIGN, false, PO>);
   void *args[] = {&p};
   const size_t dyn = size_t(2 * C::kStage + C::kXChunks) * 16 + 2 * C::kNCst * C::kBT * 4;
   if (dyn > 65536) {
@@ -772,13 +794,21 @@ template <int ROLE, bool BF16, int D, bool CAUSAL>
 hipError_t launch_bwd_masks(const BwdArgs &a, hipStream_t s) {
   // Only the key-gradient role varies g along a block's rows.
   const bool gsign = ROLE == ROLE_DK && a.dkl != nullptr;
+  constexpr bool kDK = ROLE == ROLE_DK && BF16;
+  const bool po = kDK && bwd_dk_paired(a.bh, a.nq, a.nk, a.bf16);
   switch (a.grad_mask) {
-    case 1: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, true>(a, s)
-                         : launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, false>(a, s);
-    case 2: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, true>(a, s)
-                         : launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, false>(a, s);
-    default: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, true>(a, s)
-                          : launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, false>(a, s);
+    case 1: return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, true, false>(a, s)
+                         : launch_bwd_t<BF16, D, CAUSAL, ROLE, 1, false, false>(a, s);
+    case 2:
+      if (po) return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, true, kDK>(a, s)
+                           : launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, false, kDK>(a, s);
+      return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, true, false>(a, s)
+                   : launch_bwd_t<BF16, D, CAUSAL, ROLE, 2, false, false>(a, s);
+    default:
+      if (po) return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, true, kDK>(a, s)
+                           : launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, false, kDK>(a, s);
+      return gsign ? launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, true, false>(a, s)
+                   : launch_bwd_t<BF16, D, CAUSAL, ROLE, 3, false, false>(a, s);
   }
 }
 

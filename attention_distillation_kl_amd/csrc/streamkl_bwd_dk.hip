@@ -1,7 +1,7 @@
 // streamkl_bwd_dk.hip -- key-gradient kernel of the recompute backward: each
-// workgroup owns a block of key rows (64 in the paired bf16 form) and streams
-// query tiles from its causal frontier to N_Q, accumulating dK1, dK2 in
-// registers (see streamkl_bwd.h).
+// workgroup owns a block of key rows (256 for bf16, 64 in the paired form
+// that small grids take) and streams query tiles from its causal frontier to
+// N_Q, accumulating dK1, dK2 in registers (see streamkl_bwd.h).
 #include "streamkl_bwd.h"
 
 namespace streamkl {

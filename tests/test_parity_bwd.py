@@ -99,6 +99,26 @@ def test_bwd_single_configuration_masks(mask, d, causal):
             assert part[n] is None
 
 
+def test_bwd_single_configuration_masks_on_a_large_grid():
+    """16 heads of 8192 causal tokens: the key-gradient role takes its
+    unpaired layout (256-key workgroups, at least two rounds of them, long
+    query streams).  Each single configuration must still give the full
+    backward's tensors bit for bit, and one head is checked against the
+    oracle."""
+    B, H, N, d = 1, 16, 8192, 128
+    q1, k1, q2, k2 = make_inputs(B, H, N, N, d, torch.bfloat16, "student", 0.2, seed=18, device=DEV)
+    scale = d ** -0.5
+    _, full = fwd_bwd(q1, k1, q2, k2, scale, True)
+    for mask, keep in ((1, ("dq1", "dk1")), (2, ("dq2", "dk2"))):
+        _, part = fwd_bwd(q1, k1, q2, k2, scale, True, mask=mask)
+        for n in keep:
+            assert torch.equal(part[n], full[n]), (mask, n)
+    hh = H - 1
+    ref = oracle_heads(q1, k1, q2, k2, scale, True, [hh], grads=True)[hh]
+    for n in NAMES:
+        check_grad(to64(full[n][0, hh]), ref[n], q1.dtype, f"16x8192 head {hh} {n}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_bwd_identical_teacher_student_gives_zero_gradients(dt):
     q, k, _, _ = make_inputs(1, 2, 150, 150, 64, DT[dt], "iid", 0, seed=13, device=DEV)
