@@ -62,10 +62,11 @@ class Workload:
 
     def bwd_bytes(self, kernel: str) -> float:
         """Algorithmic HBM bytes of one backward kernel: the four inputs and
-        16 B per query row (KL, LSE1, LSE2, upstream gradient) read, its two
-        gradients written ('bwd_dk': dK1, dK2; 'bwd_dq': dQ1, dQ2)."""
+        16 B per query row (KL, LSE1, LSE2, upstream gradient) read, its
+        gradients written ('bwd_dk': dK1, dK2; 'bwd_dq': dQ1, dQ2;
+        'bwd_fused': all four)."""
         bh = self.B * self.H
-        rows = self.NK if kernel == "bwd_dk" else self.NQ
+        rows = {"bwd_dk": self.NK, "bwd_dq": self.NQ, "bwd_fused": self.NQ + self.NK}[kernel]
         return float(bh * (2 * (self.NQ + self.NK) * self.d * self.elem_bytes() + 16 * self.NQ
                            + 2 * rows * self.d * self.elem_bytes()))
 
@@ -82,6 +83,9 @@ WORKLOADS = {
     "h32k": Workload("h32k", 1, 32, 32768, 32768, 128, "bf16", True, "student", 0.2, 1032, "fwd+bwd"),
     # one decoding row per head over 64K keys (the split-K forward's case)
     "decode": Workload("decode", 1, 32, 1, 65536, 128, "bf16", False, "iid", 0.0, 1006, "fwd"),
+    # a short query block over 64K keys, forward and backward (the split-K
+    # forward and the fused backward)
+    "shortq": Workload("shortq", 1, 32, 64, 65536, 128, "bf16", False, "student", 0.2, 1064, "fwd+bwd"),
 }
 
 

@@ -106,11 +106,12 @@ def streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, causal=Fa
 
 
 def streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, causal=False,
-                       grad_mask=_lib.GRAD_ALL, workspace=None):
+                       grad_mask=_lib.GRAD_ALL, workspace=None, out=None):
     """The single-pass backward (bf16 only): (dq1, dk1, dq2, dk2) as
     streamkl_bwd returns them.  ``workspace``: a device tensor of at least
     streamkl_bwd_fused_workspace_size bytes (the fp32 query-gradient sums);
-    allocated here when None."""
+    allocated here when None.  ``out``: preallocated (dq1, dk1, dq2, dk2),
+    None for unrequested gradients."""
     B, H, NQ, NK, d = _check_inputs(q1, k1, q2, k2)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q1.device
@@ -120,10 +121,10 @@ def streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, cau
     if dkl is not None:
         dkl = dkl.to(device=dev, dtype=torch.float32).expand(B, H, NQ).contiguous()
     g1, g2 = bool(grad_mask & 1), bool(grad_mask & 2)
-    dq1 = torch.empty_like(q1) if g1 else None
-    dk1 = torch.empty_like(k1) if g1 else None
-    dq2 = torch.empty_like(q2) if g2 else None
-    dk2 = torch.empty_like(k2) if g2 else None
+    if out is None:
+        out = (torch.empty_like(q1) if g1 else None, torch.empty_like(k1) if g1 else None,
+               torch.empty_like(q2) if g2 else None, torch.empty_like(k2) if g2 else None)
+    dq1, dk1, dq2, dk2 = out
     dt = _dtype_code(q1)
     need = _lib.bwd_fused_workspace_size(B, H, NQ, NK, d, int(bool(causal)), dt, grad_mask)
     if workspace is None:

@@ -30,6 +30,7 @@ KERNEL_SOURCES = {
     "fwd": ["streamkl_fwd.hip", "streamkl_device.h", "streamkl_launch.h"],
     "bwd_dk": ["streamkl_bwd.h", "streamkl_bwd_dk.hip", "streamkl_device.h", "streamkl_launch.h"],
     "bwd_dq": ["streamkl_bwd.h", "streamkl_bwd_dq.hip", "streamkl_device.h", "streamkl_launch.h"],
+    "bwd_fused": ["streamkl_bwd_fused.hip", "streamkl_device.h", "streamkl_launch.h"],
 }
 
 
@@ -271,9 +272,10 @@ def roofline_bound(w, kernel, peak_tflops):
     recomputed score products (4 d) and the four gradient products (8 d).
     Each of its two kernels forms two of the gradients, so each is credited
     half of that, 6 d; the second recompute the two-kernel form executes is
-    not algorithmic work (see executed_flops)."""
+    not algorithmic work (see executed_flops).  The fused backward (short
+    query blocks) forms all four gradients in one kernel: 12 d."""
     fwd_fl = w.fwd_flops()
-    flops = fwd_fl if kernel == "fwd" else 1.5 * fwd_fl
+    flops = {"fwd": 1.0, "bwd_dk": 1.5, "bwd_dq": 1.5, "bwd_fused": 3.0}[kernel] * fwd_fl
     nbytes = w.fwd_bytes() if kernel == "fwd" else w.bwd_bytes(kernel)
     if flops / nbytes < peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
         return "hbm", nbytes, PEAK_HBM_GBS, "GB/s"
@@ -282,10 +284,10 @@ def roofline_bound(w, kernel, peak_tflops):
 
 def executed_flops(w, kernel):
     """MFMA flops one launch of the kernel executes: the forward's 4 d per
-    pair; each backward kernel recomputes both score blocks (4 d) and forms
-    two gradients (4 d), 8 d per pair."""
+    pair; each two-kernel backward kernel recomputes both score blocks (4 d)
+    and forms two gradients (4 d), 8 d per pair; the fused backward 12 d."""
     fwd_fl = w.fwd_flops()
-    return fwd_fl if kernel == "fwd" else 2 * fwd_fl
+    return {"fwd": 1.0, "bwd_dk": 2.0, "bwd_dq": 2.0, "bwd_fused": 3.0}[kernel] * fwd_fl
 
 
 def main():
@@ -307,7 +309,7 @@ def main():
 
     import torch
     from attention_distillation_kl_amd import WORKLOADS, workload_inputs
-    from attention_distillation_kl_amd import ops
+    from attention_distillation_kl_amd import _lib, ops
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -320,9 +322,14 @@ def main():
     dq = (torch.empty_like(q1), torch.empty_like(q2))
     dk = (torch.empty_like(k1), torch.empty_like(k2))
     do_bwd = w.passes == "fwd+bwd"
-    # The backward's workspace (short query blocks only), allocated once: the
-    # query half then takes the key-partitioned path, as streamkl_bwd does.
+    # The backward's workspace (short query blocks only), allocated once.
+    # Where streamkl_bwd takes the fused form, the step runs it (one kernel
+    # and its workspace fill and conversion); otherwise the two halves, the
+    # query half with the workspace, i.e. the key-partitioned path where
+    # streamkl_bwd takes it.
     ws = ops.streamkl_bwd_workspace(q1, k1, w.causal) if do_bwd else None
+    dt = _lib.BF16 if w.dtype == "bf16" else _lib.F32
+    fused = do_bwd and _lib.bwd_fused_selected(B, H, NQ, NK, d, int(w.causal), dt, _lib.GRAD_ALL) == 1
 
     def step(ev=None):
         if ev is not None:
@@ -330,7 +337,12 @@ def main():
         kl_, l1_, l2_ = ops.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
         if ev is not None:
             ev[1].record()
-        if do_bwd:
+        if do_bwd and fused:
+            ops.streamkl_bwd_fused(q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, workspace=ws,
+                                   out=(dq[0], dk[0], dq[1], dk[1]))
+            if ev is not None:
+                ev[2].record()
+        elif do_bwd:
             ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dk)
             if ev is not None:
                 ev[2].record()
@@ -344,7 +356,7 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: {args.warmup} warmup steps done")
 
-    nev = 4 if do_bwd else 2
+    nev = (3 if fused else 4) if do_bwd else 2
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -363,7 +375,9 @@ def main():
     step_ev = sorted(e[0].elapsed_time(e[nev - 1]) for e in events)
     step_ms = median(step_ev)
     spans = {"fwd": (0, 1)}
-    if do_bwd:
+    if fused:
+        spans["bwd_fused"] = (1, 2)
+    elif do_bwd:
         spans["bwd_dk"] = (1, 2)
         spans["bwd_dq"] = (2, 3)
     kern = {k: median(e[a].elapsed_time(e[b]) for e in events) for k, (a, b) in spans.items()}

@@ -162,3 +162,18 @@ def test_roofline_credits_the_algorithmic_flops():
     assert 2 * bench.roofline_bound(h, "bwd_dk", 2500.0)[1] + bench.roofline_bound(h, "fwd", 2500.0)[1] \
         == h.fwdbwd_flops()
     assert abs(bench.roofline_bound(h, "bwd_dk", 2500.0)[1] - 1.319e13) < 1e10
+
+
+def test_short_query_backward_is_priced_in_hbm_bytes():
+    """64 queries over 64K keys: the fused backward forms all four gradients
+    (12 d flops per pair) while it reads the four inputs and writes the four
+    gradients once, about 96 flops per algorithmic byte, below the machine
+    balance: it is priced in bytes against the HBM bandwidth."""
+    sys.path.insert(0, ROOT)
+    import bench
+    w = WORKLOADS["shortq"]
+    bound, nbytes, peak, unit = bench.roofline_bound(w, "bwd_fused", 2500.0)
+    assert (bound, peak, unit) == ("hbm", 8000.0, "GB/s")
+    per_head = 2 * (64 + 65536) * 128 * 2 + 16 * 64 + 2 * (64 + 65536) * 128 * 2
+    assert nbytes == 32 * per_head
+    assert bench.executed_flops(w, "bwd_fused") == 12 * 32 * 64 * 65536 * 128
