@@ -102,6 +102,32 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Head and length rank (0 = the most work) of logical workgroup `bid` of a
+// causal grid of n = heads * nblk workgroups, nblk per head, whose blocks of
+// rank r all do about the same work and rank 0 the most.  The XCD that runs
+// logical ids [x per, (x + 1) per), per = n / 8, holds whole heads when per
+// is a multiple of nblk: there the ids take the ranks in order, each rank
+// over the XCD's heads in turn, so the longest blocks of all its heads start
+// first and the short ones fill the end.  Taking one head after the other,
+// when a head has fewer blocks than an XCD has resident workgroups, starts
+// the long blocks of its last heads late (32 blocks a head, 64 resident, 4
+// heads per XCD: list scheduling finishes at 1.5x the ideal time).  The
+// cost: more heads share each XCD's L2 at a time.  Otherwise: head-major,
+// rank order within a head.
+struct BlockPos {
+  int bh, rank;
+};
+__device__ __forceinline__ BlockPos longest_first(int bid, int n, int nblk) {
+  const int per = n >> 3;
+  if (bid < (per << 3) && per % nblk == 0) {
+    const int g = per / nblk;  // heads per XCD
+    const int base = bid - bid % per;
+    const int pos = bid - base;
+    return {base / nblk + pos % g, pos / g};
+  }
+  return {bid / nblk, bid % nblk};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // NaN-propagating maximum (IEEE 754-2019 maximum).  gfx950 executes it

@@ -72,6 +72,9 @@ struct FwdParams {
   // Split-K: the key tiles are dealt to nsplit partitions of tps tiles each;
   // partition states go to part = [5][nsplit][bh * nq] (m1, m2, l1, l2, acc).
   int nsplit, tps;
+  // Causal, unsplit: the query blocks' ranks are taken over each XCD's heads
+  // (longest_first) instead of head by head.
+  int lf;
   size_t rows;  // B * H * N_Q
   float *part;
 };
@@ -98,16 +101,22 @@ void fwd_kernel(FwdParams p) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
 
-  // Heads are contiguous in logical order (one head per XCD at a time);
-  // for causal problems the longest query blocks of a head go first.
+  // Heads are contiguous in logical order (one head per XCD at a time); for
+  // causal problems the longest query blocks of a head go first, or, with
+  // p.lf, the longest of all the XCD's heads (longest_first).
   // With split-K, the query blocks of one (head, partition) are consecutive,
   // so they share the partition's K tiles in one L2.
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_bh = p.nqb * (SPLIT ? p.nsplit : 1);
-  const int bh = bid / per_bh;
+  int bh = bid / per_bh;
   const int rem = bid - bh * per_bh;
   const int split = SPLIT ? rem / p.nqb : 0;
-  const int qbr = rem - split * p.nqb;
+  int qbr = rem - split * p.nqb;
+  if (CAUSAL && !SPLIT && p.lf) {
+    const BlockPos bp = longest_first(bid, gridDim.x, p.nqb);
+    bh = bp.bh;
+    qbr = bp.rank;
+  }
   const int qb = CAUSAL ? p.nqb - 1 - qbr : qbr;
   const int q0 = qb * C::kBQ;
   // The wave's query block and, with kKSplit > 1, which 32-key blocks of a
@@ -483,6 +492,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
   lse2[r] = l2;
 }
 
+// Whether the causal, unsplit forward takes its query blocks' ranks over each
+// XCD's heads (longest_first): where a head has fewer query blocks than an
+// XCD has resident workgroups (two per CU, 32 CUs) -- only then does taking
+// the heads one after the other leave long blocks for the end -- and each
+// XCD's share of the grid is whole heads.  Measured at 64 heads x 32 query
+// blocks: -11%; at 128 blocks a head, where it would not help, the shared L2
+// made it 2-4% slower.
+inline bool fwd_longest_first(long long nwg, long long nqb) {
+  constexpr long long kResidentPerXcd = 2 * 32;
+  const long long per = nwg / 8;
+  return nqb < kResidentPerXcd && per > 0 && per % nqb == 0;
+}
+
 template <bool BF16, int D, bool CAUSAL, bool RM = false>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   using C = FwdCfg<BF16, D, RM>;
@@ -505,6 +527,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   p.nsplit = split ? a.splits : 1;
   p.tps = (total_tiles + p.nsplit - 1) / p.nsplit;
   p.part = a.part;
+  p.lf = (CAUSAL && !split && fwd_longest_first((long long)p.nqb * a.bh, p.nqb)) ? 1 : 0;
   const long long blocks = (long long)p.nqb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
@@ -529,12 +552,19 @@ int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal) {
   // to 20% more for short query blocks, since each workgroup also pays its
   // fragment loads and state stores.)  Causal problems with N_Q > N_K / 2
   // are uneven: the causal triangle makes the query blocks' work differ up
-  // to N_Q / 256 fold, so they also get partitions of at least 16 tiles for
-  // about four rounds, which lets the workgroups balance (measured 5-17%
-  // faster at 4K-8K tokens).  The larger of the two counts is taken.
+  // to N_Q / 256 fold.  Over more than one round, the unsplit kernel
+  // balances them by taking the longest blocks of each XCD's heads first,
+  // where it can (fwd_longest_first; measured 0.58 ms unsplit against 0.70
+  // in two partitions at 32 heads x 8K tokens, 0.30 against 0.38 at 64 x
+  // 4K).  Within one round, or where it cannot, they get partitions of at
+  // least 16 tiles for about four rounds, which lets the workgroups balance
+  // (measured 5-17% faster at 4K-8K tokens than one partition taken head by
+  // head; 0.23 against 0.24 ms at 32 x 4K with the blocks sorted).  The
+  // larger of the two counts is taken.
   const bool nqb2 = bf16 || d == 64;
   const int kbq = nqb2 ? 256 : 128, kbk = bf16 ? 64 : 32;
-  const long long nwg = (long long)bh * ((nq + kbq - 1) / kbq);
+  const long long nqb = (nq + kbq - 1) / kbq;
+  const long long nwg = (long long)bh * nqb;
   if (nwg <= 0) return 1;
   const long long tiles = (nk + kbk - 1) / kbk;
   auto count = [&](long long target, long long min_tiles) {
@@ -542,7 +572,8 @@ int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal) {
     return std::min((target + nwg - 1) / nwg, std::max(1LL, tiles / min_tiles));
   };
   long long s = count(2 * 256, 4);
-  if (causal && 2LL * nq > nk) s = std::max(s, count(8 * 256, 16));
+  if (causal && 2LL * nq > nk && (nwg <= 2 * 256 || !fwd_longest_first(nwg, nqb)))
+    s = std::max(s, count(8 * 256, 16));
   return int(std::min(s, 256LL));
 }
 

@@ -165,6 +165,36 @@ def test_fwd_logits_that_rise_or_fall_along_the_keys(dt, direction, causal):
     assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", [1, -1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_teacher_and_student_maxima_far_apart(dt, direction, causal):
+    """The keys of the ramp test above, with the teacher's queries along u in
+    every row but the student's only in even rows: in odd rows the student's
+    logits stay near unit scale while the teacher's climb (or start) hundreds
+    of log2 units above them, so the teacher's shift is raised on every block
+    (rising logits) while the student's must stay near its own maximum, or
+    its terms underflow to zero.  Every wave holds rows of both kinds.  Same
+    bound as the ramp test."""
+    g = torch.Generator(device=DEV).manual_seed(78)
+    NQ, NK, d = 96, 700, 64
+    u = torch.randn(d, device=DEV, generator=g)
+    u = u / u.norm()
+    ramp = torch.arange(NK, device=DEV, dtype=torch.float32)
+    if direction < 0:
+        ramp = ramp.flip(0)
+    def keys():
+        return (ramp[:, None] / 8.0) * u + 0.3 * torch.randn(NK, d, device=DEV, generator=g)
+    q1 = 12.0 * u + 0.3 * torch.randn(NQ, d, device=DEV, generator=g)
+    q2 = 0.3 * torch.randn(NQ, d, device=DEV, generator=g)
+    q2[0::2] += 12.0 * u
+    q1, k1, q2, k2 = (x[None, None].to(DT[dt]).contiguous() for x in (q1, keys(), q2, keys()))
+    kl, l1, l2, _ = run_and_compare(q1, k1, q2, k2, 1.0, causal, tag=f"apart {direction}", by_magnitude=True)
+    assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
+    gap = (l1 - l2)[0, 0].abs().cpu()
+    assert (gap[1::2] > 64 * math.log(2)).all()   # odd rows: the maxima really are far apart
+
+
 # KL / LSE rounding when every score is exact in fp32 (multiple of 2^-24
 # |LSE_ref|).  Left: one rounding each in the exponent's shift -m c, in
 # m * scale, in m * scale + log l and in the lane-half merge; the raises'
