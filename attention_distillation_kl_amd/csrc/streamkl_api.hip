@@ -134,11 +134,11 @@ int streamkl_bwd_fused_selected(int B, int H, int N_Q, int N_K, int d, int causa
   if (dtype != STREAMKL_BF16 || grad_mask < 1 || grad_mask > 3 || (long long)B * H > INT32_MAX) return 0;
   if (causal && N_Q > N_K) return 0;
   // Short query blocks only, where the fused form measured faster than the
-  // two-kernel form: up to one 64-row query tile per head at d = 128 (slower
-  // from 96 queries); at d = 64, whose dQ products add twice the atomics per
-  // flop, up to 8 queries (slower at 32).  And the fp32 query-gradient buffer
-  // within L2, the page's criterion.
-  if (N_Q > (d == 128 ? 64 : 8)) return 0;
+  // two-kernel form: one 64-row query tile per head, which a workgroup keeps
+  // while it walks its key blocks (1.0-2.3x at d = 128 and d = 64; slower
+  // from 96 queries, with a second tile).  And the fp32 query-gradient
+  // buffer within L2, the page's criterion.
+  if (N_Q > 64) return 0;
   return streamkl::bwd_fused_workspace_floats(B * H, N_Q, d, grad_mask) * sizeof(float) <= kL2Bytes ? 1 : 0;
 }
 

@@ -34,6 +34,19 @@
 //     consecutive columns of two rows, i.e. two 128-byte lines;
 //   * the fp32 buffer is zeroed by a fill kernel before and converted to the
 //     gradient's element type (times f_t) by a second kernel after.
+// With one query tile per head (N_Q <= 64, the sizes streamkl_bwd sends
+// here) the kernel takes a second form, which turns the per-block chain of
+// copy, barrier, products and atomics into a pipeline:
+//   * a workgroup loads the query tile and its row constants once and walks
+//     up to 16 consecutive key blocks; each block's stationary tiles are
+//     copied (out of the compiler's sight, waited for explicitly) while the
+//     previous block is worked on;
+//   * the e values stay packed in registers after the scores, and dK is
+//     formed one 32-column slice of d at a time, each slice stored as soon
+//     as it is complete: 32 accumulator registers instead of 128;
+//   * which leaves room to sum each wave's dQ blocks over all of the
+//     workgroup's key blocks in registers: one round of atomics per
+//     workgroup instead of one per key block.
 // The order of the atomic additions varies from run to run, so dQ is not
 // bitwise reproducible (dK is).
 #include "streamkl_device.h"
@@ -76,6 +89,14 @@ struct FusedCfg {
   static constexpr int kOffX = kOffStage1;
   static constexpr int kLdsBytes = kOffE + 2 * kEBytes;
   static_assert(kOffX + 2 * kXChunks * 16 <= kLdsBytes, "stationary tiles must fit the shared space");
+  // One query tile for the whole workgroup (N_Q <= kBT), which walks several
+  // key blocks: no second query stage; the e buffers take its place and the
+  // stationary tiles get space of their own, so that the next block's copies
+  // overlap the current block's work.
+  static constexpr int kOffEM = kOffStage1;
+  static constexpr int kOffXM = kOffEM + 2 * kEBytes;
+  static constexpr int kLdsBytesM = kOffXM + 2 * kXChunks * 16;
+  static_assert(kLdsBytesM <= 160 * 1024, "LDS budget");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kTileChunks % kThreads == 0 && kXChunks % kThreads == 0, "tiles split evenly");
   static_assert(kWaves % kMB == 0, "d slices split the waves evenly");
@@ -87,6 +108,7 @@ struct FusedParams {
   char *dk1, *dk2;
   float *ws1, *ws2;   // fp32 query-gradient sums [bh][N_Q][d], zero on entry
   int nq, nk, nsb;    // nsb: stationary blocks per head
+  int kbpw;           // key blocks per workgroup (the one-tile form; 1 otherwise)
   float scale, c, inv_scale;
 };
 
@@ -99,7 +121,7 @@ __device__ __forceinline__ int ebyte(int key, int q) {
   return key * 128 + (((q >> 3) ^ (key & 7)) << 4) + (q & 7) * 2;
 }
 
-template <int D, bool CAUSAL, int MASK, bool GSIGN>
+template <int D, bool CAUSAL, int MASK, bool GSIGN, bool MULTI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fused_bwd_kernel(FusedParams p) {
   using C = FusedCfg<D>;
@@ -112,51 +134,71 @@ void fused_bwd_kernel(FusedParams p) {
   float (*cstage)[4 * C::kBT] = reinterpret_cast<float (*)[4 * C::kBT]>(lbase);
   u32x4 *ystage0 = reinterpret_cast<u32x4 *>(lbase + C::kOffStage0);
   u32x4 *ystage1 = reinterpret_cast<u32x4 *>(lbase + C::kOffStage1);
-  char *ebuf = lbase + C::kOffE;  // [tensor][key][query] bf16, swizzled
-  u32x4 *xtile = reinterpret_cast<u32x4 *>(lbase + C::kOffX);
+  char *ebuf = lbase + (MULTI ? C::kOffEM : C::kOffE);  // [tensor][key][query] bf16, swizzled
+  u32x4 *xtile = reinterpret_cast<u32x4 *>(lbase + (MULTI ? C::kOffXM : C::kOffX));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int s16 = lane & 15, grp = lane >> 4;
 
+  // Workgroup g of a head takes key blocks [g kbpw, min((g + 1) kbpw, nsb)),
+  // key block 0 first: with the mask it sees the most queries.
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = bid / p.nsb;
-  const int sblk = bid - bh * p.nsb;  // key block 0 first: with the mask it sees the most queries
-  const int s0 = sblk * C::kBS;
-  const int w0 = s0 + wave * 32;
-  const int srow = w0 + col;           // the lane's key
+  const int kbpw = MULTI ? p.kbpw : 1;
+  const int ngrp = (p.nsb + kbpw - 1) / kbpw;
+  const int bh = bid / ngrp;
+  const int blk0 = (bid - bh * ngrp) * kbpw;
+  const int blk1 = min(blk0 + kbpw, p.nsb);
   const int off = p.nk - p.nq;
 
   const size_t koff = size_t(bh) * p.nk * G::kRowBytes;
   const char *Y1 = p.q1 + size_t(bh) * p.nq * G::kRowBytes;
   const char *Y2 = p.q2 + size_t(bh) * p.nq * G::kRowBytes;
 
-  // Streamed query range: from the workgroup's causal frontier to N_Q.
-  const int t_begin = CAUSAL ? max(0, s0 - off) : 0;
-  const int tile0 = t_begin / C::kBT;
-  const int tile1 = (p.nq + C::kBT - 1) / C::kBT;
-  const int ntiles = max(tile1 - tile0, 0);
-  // First admissible query of the lane's key, and whether its key exists.
-  const int lim = CAUSAL ? max(srow - off, 0) : 0;
-  const bool keys_past_end = w0 + 31 >= p.nk;  // wave-uniform
+  // The wave's keys in key block kb: the first one (w0), the lane's (srow),
+  // its first admissible query (lim), and whether any of the wave's keys is
+  // past N_K (wave-uniform).
+  struct Blk {
+    int s0, w0, srow, lim;
+    bool keys_past_end;
+  };
+  auto blk_state = [&](int kb) {
+    Blk b;
+    b.s0 = kb * C::kBS;
+    b.w0 = b.s0 + wave * 32;
+    b.srow = b.w0 + col;
+    b.lim = CAUSAL ? max(b.srow - off, 0) : 0;
+    b.keys_past_end = b.w0 + 31 >= p.nk;
+    return b;
+  };
 
-  // Stationary key tiles -> LDS (rows past N_K repeat the last one; their e
-  // values are zero).  The score products' key fragments and the dQ
-  // products' key columns are both read from them, so each key row is
-  // fetched from memory once.
-  {
-    const char *K1 = p.k1 + koff, *K2 = p.k2 + koff;
+  // Stationary key tiles of block kb -> LDS (rows past N_K repeat the last
+  // one; their e values are zero).  The score products' key fragments and
+  // the dQ products' key columns are both read from them, so each key row
+  // is fetched from memory once.
+  // `unseen`: copies issued out of the compiler's sight (dma16_unseen); the
+  // caller waits for them (vmcnt0_wait) before the barrier that publishes
+  // the tiles.
+  auto load_x = [&](int kb, auto unseen_c) {
+    const int s0 = kb * C::kBS;
+    const char *K1 = p.k1 + koff + size_t(s0) * G::kRowBytes;
+    const char *K2 = p.k2 + koff + size_t(s0) * G::kRowBytes;
 #pragma unroll
     for (int i = 0; i < C::kXLoads; ++i) {
       const int pos = i * C::kThreads + tid;
       const int row = pos / G::kChunks;
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
-      const size_t o = size_t(min(s0 + row, p.nk - 1)) * G::kRowBytes + ch * 16;
-      dma16(K1 + o, xtile + i * C::kThreads + wave * 64);
-      dma16(K2 + o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
+      const uint32_t o = uint32_t(min(s0 + row, p.nk - 1) - s0) * G::kRowBytes + ch * 16;
+      if constexpr (decltype(unseen_c)::value) {
+        dma16_unseen(K1, o, xtile + i * C::kThreads + wave * 64);
+        dma16_unseen(K2, o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
+      } else {
+        dma16(K1 + o, xtile + i * C::kThreads + wave * 64);
+        dma16(K2 + o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
+      }
     }
-  }
+  };
 
   auto issue = [&](int tile, int stage) {
     u32x4 *wbase = (stage ? ystage1 : ystage0) + wave * 64;
@@ -192,23 +234,18 @@ void fused_bwd_kernel(FusedParams p) {
     }
   };
 
-  if (ntiles > 0) {
-    issue(tile0, 0);
-    cwrite(tile0, 0);
-  }
-  __syncthreads();  // the stationary tiles, the first query tile and its constants
-
-  // K_t fragments of the dQ products (B operand: lane = column of d, 8 keys
-  // per half), read once from the stationary tiles with transposing reads.
-  // Key order within a 16-key step: position 4t + j holds key
-  // 16 ks + 8 t + 4 h + j, the order the e buffer reads below use as well.
+  // Key fragments of the score products (B operand: lane = key, the chunks
+  // of its half of d) and the K_t fragments of the dQ products (B operand:
+  // lane = column of d, 8 keys per half), read from the stationary tiles
+  // (transposing reads for the latter).  Key order within a 16-key step:
+  // position 4t + j holds key 16 ks + 8 t + 4 h + j, the order the e buffer
+  // reads below use as well.  A key past N_K reads the repeated last row;
+  // its scores are masked.
   const int mb = wave % kMB;
   const int kg = wave / kMB;
-  // Key fragments of the score products (B operand: lane = key, the chunks
-  // of its half of d).  A key past N_K reads the repeated last row; its
-  // scores are masked.
   u32x4 xf1[G::kLaneChunks], xf2[G::kLaneChunks];
-  {
+  u32x4 kt1[C::kKSteps], kt2[C::kKSteps];
+  auto read_frags = [&]() {
     const int xrow = wave * 32 + col;
 #pragma unroll
     for (int cc = 0; cc < G::kLaneChunks; ++cc) {
@@ -216,9 +253,6 @@ void fused_bwd_kernel(FusedParams p) {
       xf1[cc] = xtile[pos];
       xf2[cc] = xtile[C::kXChunks + pos];
     }
-  }
-  u32x4 kt1[C::kKSteps], kt2[C::kKSteps];
-  {
     const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
 #pragma unroll
     for (int ks = 0; ks < C::kKSteps; ++ks) {
@@ -238,24 +272,20 @@ void fused_bwd_kernel(FusedParams p) {
         }
       }
     }
-  }
-  __syncthreads();  // everyone has its fragments: the space is free for stage 1 and the e buffers
+  };
 
   f32x16 acc1[kMB], acc2[kMB];
-#pragma unroll
-  for (int m = 0; m < kMB; ++m) {
-    acc1[m] = f32x16{};
-    acc2[m] = f32x16{};
-  }
   const float c = p.c;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int tile = tile0 + it;
-    const int stage = it & 1;
-    if (it + 1 < ntiles) issue(tile + 1, stage ^ 1);
+  // Steps 1-4 for the query tile `tile` (in LDS stage `stage`) and the keys
+  // of block B: scores, e values, dK_t^T += Q_t^T e_t, e values to the
+  // buffer.  Without `grad_c` step 3 is left out and the packed e values
+  // are kept in `pks` [32-query block][tensor][16-query step] instead.
+  using PackedE = u32x4[C::kSub][2][2];
+  auto tile_work = [&](int tile, int stage, const Blk &B, auto grad_c, PackedE &pks) {
+    constexpr bool kInlineGrad = decltype(grad_c)::value;
     const u32x4 *ybase = stage ? ystage1 : ystage0;
     const float *cst = cstage[stage];
-
 #pragma unroll
     for (int sb = 0; sb < C::kSub; ++sb) {
       const int tb = tile * C::kBT + sb * 32;
@@ -275,13 +305,14 @@ void fused_bwd_kernel(FusedParams p) {
           s2[4 * g4 + q] = v2[q];
         }
       }
-      const bool straddles = keys_past_end || tb + 31 > p.nq - 1 || (CAUSAL && tb < max(w0 + 31 - off, 0));
+      const bool straddles =
+          B.keys_past_end || tb + 31 > p.nq - 1 || (CAUSAL && tb < max(B.w0 + 31 - off, 0));
       if (straddles) {
         const int rel = tb + 4 * h;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = rel + c_row(r, 0);
-          const bool ok = srow < p.nk && t >= lim && t < p.nq;
+          const bool ok = B.srow < p.nk && t >= B.lim && t < p.nq;
           s1[r] = ok ? s1[r] : -1e30f;
           s2[r] = ok ? s2[r] : -1e30f;
         }
@@ -350,8 +381,16 @@ void fused_bwd_kernel(FusedParams p) {
                                                             __builtin_bit_cast(bf16x8, pk[ks]), acc[m], 0, 0, 0);
           }
       };
-      if (kG1) grad(reinterpret_cast<const char *>(ybase), pk1, acc1);
-      if (kG2) grad(reinterpret_cast<const char *>(ybase + C::kTileChunks), pk2, acc2);
+      if constexpr (kInlineGrad) {
+        if (kG1) grad(reinterpret_cast<const char *>(ybase), pk1, acc1);
+        if (kG2) grad(reinterpret_cast<const char *>(ybase + C::kTileChunks), pk2, acc2);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          pks[sb][0][ks] = pk1[ks];
+          pks[sb][1][ks] = pk2[ks];
+        }
+      }
       // 4. e_t -> the e buffer, row = the lane's key (within the workgroup),
       //    4 consecutive queries (32 sb + 8 g4 + 4 h ..) per store.
       {
@@ -365,52 +404,59 @@ void fused_bwd_kernel(FusedParams p) {
         }
       }
     }
-    __syncthreads();  // every wave's e blocks of this tile are in the buffer
+  };
 
-    // 5. dQ_t block (32 queries x the wave's 32 columns of d) = e_t x K_t over
-    //    the wave's key group, then added to the fp32 sums with atomics.
-    //    A operand: e_t with lane = query, 8 keys per half, by transposing
-    //    reads of the [key][query] buffer (lane (s, grp) supplies key row
-    //    16ks + 8t + 4h + s/4, queries 32sb + 16(grp&1) + 4(s&3) .. +3).
+  // 5. dQ_t block (32 queries x the wave's 32 columns of d) = e_t x K_t over
+  //    the wave's key group, added to `a`.  A operand: e_t with lane =
+  //    query, 8 keys per half, by transposing reads of the [key][query]
+  //    buffer (lane (s, grp) supplies key row 16ks + 8t + 4h + s/4, queries
+  //    32sb + 16(grp&1) + 4(s&3) .. +3).
+  auto dq_product = [&](int sb, const char *eb, const u32x4 (&kt)[C::kKSteps], f32x16 a) {
+    const int qa = sb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < C::kKSteps; ++ks) {
+      u32x4 e;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
+        const u32x2 v = read_tr(eb + ebyte(key, qa));
+        e[2 * t] = v[0];
+        e[2 * t + 1] = v[1];
+      }
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), __builtin_bit_cast(bf16x8, kt[ks]),
+                                                  a, 0, 0, 0);
+    }
+    return a;
+  };
+  // The fp32 sums += a, with atomics.  a[r]: query tile*64 + 32 sb +
+  // c_row(r, h), column mb*32 + col.  The row offset is made opaque to the
+  // compiler, so that the 16 addresses are formed here rather than kept
+  // live (as 32 registers) across the one-tile form's loop over key blocks.
+  auto dq_atomics = [&](int tile, int sb, const f32x16 &a, float *ws) {
+    const int qb = tile * C::kBT + sb * 32;
+    size_t rowoff = (size_t(bh) * p.nq + qb) * D + mb * 32 + col;
+    asm volatile("" : "+v"(rowoff));
+    float *base = ws + rowoff;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = c_row(r, h);
+      if (qb + q < p.nq) unsafeAtomicAdd(base + size_t(q) * D, a[r]);
+    }
+  };
+  auto tile_dq = [&](int tile) {
 #pragma unroll
     for (int sb = 0; sb < C::kSub; ++sb) {
-      if (tile * C::kBT + sb * 32 >= p.nq) continue;  // skipped above as well
-      const int qa = sb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
-      auto dq_block = [&](const char *eb, const u32x4 (&kt)[C::kKSteps], float *ws) {
-        f32x16 a = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::kKSteps; ++ks) {
-          u32x4 e;
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int key = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
-            const u32x2 v = read_tr(eb + ebyte(key, qa));
-            e[2 * t] = v[0];
-            e[2 * t + 1] = v[1];
-          }
-          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), __builtin_bit_cast(bf16x8, kt[ks]),
-                                                      a, 0, 0, 0);
-        }
-        // a[r]: query tile*64 + 32 sb + c_row(r, h), column mb*32 + col.
-        const int qb = tile * C::kBT + sb * 32;
-        float *base = ws + (size_t(bh) * p.nq + qb) * D + mb * 32 + col;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = c_row(r, h);
-          if (qb + q < p.nq) unsafeAtomicAdd(base + size_t(q) * D, a[r]);
-        }
-      };
-      if (kG1) dq_block(ebuf, kt1, p.ws1);
-      if (kG2) dq_block(ebuf + C::kEBytes, kt2, p.ws2);
+      if (tile * C::kBT + sb * 32 >= p.nq) continue;  // skipped in tile_work as well
+      if (kG1) dq_atomics(tile, sb, dq_product(sb, ebuf, kt1, f32x16{}), p.ws1);
+      if (kG2) dq_atomics(tile, sb, dq_product(sb, ebuf + C::kEBytes, kt2, f32x16{}), p.ws2);
     }
+  };
 
-    if (it + 1 < ntiles) cwrite(tile + 1, stage ^ 1);
-    __syncthreads();  // the next tile's copies and constants; the e buffer is free again
-  }
-
-  // dK write-out: dK1 = scale^2 acc1, dK2 = scale acc2 (g is inside e).
-  if (srow < p.nk) {
-    const size_t ro = koff + size_t(srow) * G::kRowBytes;
+  // dK write-out of block B: dK1 = scale^2 acc1, dK2 = scale acc2 (g is
+  // inside e).
+  auto store_dk = [&](const Blk &B) {
+    if (B.srow >= p.nk) return;
+    const size_t ro = koff + size_t(B.srow) * G::kRowBytes;
     auto store = [&](char *O, float f, const f32x16 (&A)[kMB]) {
 #pragma unroll
       for (int m = 0; m < kMB; ++m)
@@ -423,7 +469,137 @@ void fused_bwd_kernel(FusedParams p) {
     };
     if (kG1) store(p.dk1, p.scale * p.scale, acc1);
     if (kG2) store(p.dk2, p.scale, acc2);
+  };
+  // The one-tile form's dK of block B (query tile in stage 0): dK_t^T =
+  // Q_t^T e_t from the packed e values, one tensor and two 32-column slices
+  // of d at a time, each pair written out as soon as it is complete: 32
+  // accumulator registers instead of 128, and every store burst covers whole
+  // 128-byte lines of the key rows (64-byte halves written apart measured
+  // 0.35 GB of extra HBM writes at 64 queries x 64K keys x 32 heads).  Each
+  // slice's products run in the order step 3 takes them, so the results are
+  // the same bits.
+  auto dk_by_slices = [&](const Blk &B, const PackedE &pks) {
+    const size_t ro = koff + size_t(min(B.srow, p.nk - 1)) * G::kRowBytes;
+    auto tensor = [&](int t, const char *yb, char *O, float f) {
+#pragma unroll
+      for (int mp = 0; mp < kMB; mp += 2) {
+        f32x16 a[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int sb = 0; sb < C::kSub; ++sb) {
+          if (sb * 32 >= p.nq) continue;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int d0 = (mp + j) * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
+              u32x4 fq;
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt) {
+                const int row = sb * 32 + 16 * ks + 8 * tt + 4 * h + (s16 >> 2);
+                const u32x2 v = read_tr(yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2);
+                fq[2 * tt] = v[0];
+                fq[2 * tt + 1] = v[1];
+              }
+              a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fq),
+                                                             __builtin_bit_cast(bf16x8, pks[sb][t][ks]), a[j], 0, 0, 0);
+            }
+        }
+        if (B.srow < p.nk) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int dc = (mp + j) * 32 + g4 * 8 + 4 * h;
+              *reinterpret_cast<u32x2 *>(O + ro + dc * 2) =
+                  u32x2{pack_bf16(a[j][4 * g4] * f, a[j][4 * g4 + 1] * f), pack_bf16(a[j][4 * g4 + 2] * f, a[j][4 * g4 + 3] * f)};
+            }
+        }
+      }
+    };
+    if (kG1) tensor(0, reinterpret_cast<const char *>(ystage0), p.dk1, p.scale * p.scale);
+    if (kG2) tensor(1, reinterpret_cast<const char *>(ystage0 + C::kTileChunks), p.dk2, p.scale);
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int m = 0; m < kMB; ++m) {
+      acc1[m] = f32x16{};
+      acc2[m] = f32x16{};
+    }
+  };
+
+  if constexpr (MULTI) {
+    // One query tile (N_Q <= kBT: every key block's causal frontier lies in
+    // it), loaded once; the key blocks follow one another, each block's
+    // stationary tiles copied while the previous block is worked on.
+    // The copies of block kb + 1 are waited for after block kb's scores,
+    // where the wait also covers block kb - 1's dK stores, issued a whole
+    // block earlier.  The dQ blocks are summed over the workgroup's key
+    // blocks in registers and added to the fp32 sums once, at the end: the
+    // atomics fall kbpw-fold.
+    if (blk0 >= blk1) return;
+    load_x(blk0, std::false_type{});
+    issue(0, 0);
+    cwrite(0, 0);
+    __syncthreads();  // the first stationary tiles, the query tile and its constants
+    f32x16 dqa1[C::kSub], dqa2[C::kSub];
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) dqa1[sb] = dqa2[sb] = f32x16{};
+    for (int kb = blk0; kb < blk1; ++kb) {
+      const Blk B = blk_state(kb);
+      read_frags();
+      __syncthreads();  // every wave has its fragments: the stationary space is free
+      if (kb + 1 < blk1) load_x(kb + 1, std::true_type{});
+      PackedE pks;
+      tile_work(0, 0, B, std::false_type{}, pks);
+      vmcnt0_wait();    // block kb + 1's stationary tiles have landed
+      __syncthreads();  // every wave's e blocks are in the buffer; so are those tiles
+      dk_by_slices(B, pks);
+#pragma unroll
+      for (int sb = 0; sb < C::kSub; ++sb) {
+        if (sb * 32 >= p.nq) continue;
+        if (kG1) dqa1[sb] = dq_product(sb, ebuf, kt1, dqa1[sb]);
+        if (kG2) dqa2[sb] = dq_product(sb, ebuf + C::kEBytes, kt2, dqa2[sb]);
+      }
+      __syncthreads();  // the e buffer is free again
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::kSub; ++sb) {
+      if (sb * 32 >= p.nq) continue;
+      if (kG1) dq_atomics(0, sb, dqa1[sb], p.ws1);
+      if (kG2) dq_atomics(0, sb, dqa2[sb], p.ws2);
+    }
+    return;
   }
+
+  const Blk B = blk_state(blk0);
+  // Streamed query range: from the workgroup's causal frontier to N_Q.
+  const int t_begin = CAUSAL ? max(0, B.s0 - off) : 0;
+  const int tile0 = t_begin / C::kBT;
+  const int tile1 = (p.nq + C::kBT - 1) / C::kBT;
+  const int ntiles = max(tile1 - tile0, 0);
+
+  load_x(blk0, std::false_type{});
+  if (ntiles > 0) {
+    issue(tile0, 0);
+    cwrite(tile0, 0);
+  }
+  __syncthreads();  // the stationary tiles, the first query tile and its constants
+  read_frags();
+  __syncthreads();  // everyone has its fragments: the space is free for stage 1 and the e buffers
+  zero_acc();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int tile = tile0 + it;
+    const int stage = it & 1;
+    if (it + 1 < ntiles) issue(tile + 1, stage ^ 1);
+    PackedE unused;
+    tile_work(tile, stage, B, std::true_type{}, unused);
+    __syncthreads();  // every wave's e blocks of this tile are in the buffer
+    tile_dq(tile);
+    if (it + 1 < ntiles) cwrite(tile + 1, stage ^ 1);
+    __syncthreads();  // the next tile's copies and constants; the e buffer is free again
+  }
+  store_dk(B);
 }
 
 // Zeroes n4 float4 values.
@@ -459,6 +635,13 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
   p.nq = a.nq;
   p.nk = a.nk;
   p.nsb = (a.nk + C::kBS - 1) / C::kBS;
+  // With one query tile, a workgroup walks up to 16 key blocks, as many as
+  // leave about two rounds of workgroups (one per CU); more tiles, or none
+  // (dK is then written as zeros): one block.
+  const bool multi = a.nq >= 1 && a.nq <= C::kBT;
+  const long long nblk = (long long)p.nsb * a.bh;
+  p.kbpw = multi ? int(std::max(1LL, std::min(16LL, nblk / (2 * 256)))) : 1;
+  const int ngrp = (p.nsb + p.kbpw - 1) / p.kbpw;
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
   p.inv_scale = float(1.0 / double(a.scale));
@@ -470,14 +653,16 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long blocks = (long long)p.nsb * a.bh;
+  const long long blocks = (long long)ngrp * a.bh;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   if (blocks > 0) {
-    const void *fn = reinterpret_cast<const void *>(&fused_bwd_kernel<D, CAUSAL, MASK, GSIGN>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    const void *fn = multi ? reinterpret_cast<const void *>(&fused_bwd_kernel<D, CAUSAL, MASK, GSIGN, true>)
+                           : reinterpret_cast<const void *>(&fused_bwd_kernel<D, CAUSAL, MASK, GSIGN, false>);
+    const int lds_bytes = multi ? C::kLdsBytesM : C::kLdsBytes;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     void *args[] = {&p};
-    e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
+    e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, lds_bytes, stream);
     if (e != hipSuccess) return e;
   }
   if (n4 > 0) {

@@ -277,8 +277,7 @@ size_t streamkl_bwd_fused_workspace_size(int B, int H, int N_Q, int N_K,
  * the page's criterion (the query-gradient buffer, one fp32 [B, H, N_Q, d]
  * array per requested gradient, fits in the 32 MiB of L2 of the eight XCDs),
  * bf16 inputs, and short query blocks where it measured faster than the
- * two-kernel form: 1 <= N_Q <= 64 at d = 128 (one query tile per head),
- * 1 <= N_Q <= 8 at d = 64; 0 otherwise.
+ * two-kernel form: 1 <= N_Q <= 64 (one query tile per head); 0 otherwise.
  */
 int streamkl_bwd_fused_selected(int B, int H, int N_Q, int N_K, int d,
                                 int causal, int dtype, int grad_mask);

@@ -202,17 +202,16 @@ def test_backward_workspace_query(lib):
 
 def test_fused_backward_selection_and_workspace(lib):
     """streamkl_bwd takes the fused form for bf16 with at most 64 queries per
-    head at d = 128 (8 at d = 64) while the fp32 query-gradient buffer fits
-    the 32 MiB of L2; its workspace is then at least one [B, H, N_Q, d] fp32
-    array per requested gradient (and still at least what the partitioned
-    query half needs)."""
+    head (one query tile) while the fp32 query-gradient buffer fits the 32
+    MiB of L2; its workspace is then at least one [B, H, N_Q, d] fp32 array
+    per requested gradient (and still at least what the partitioned query
+    half needs)."""
     sel = _lib.bwd_fused_selected
     for nq in (1, 17, 64):
         assert sel(1, 32, nq, 65536, 128, 1, _lib.BF16, 3) == 1
-    for nq in (1, 8):
         assert sel(1, 32, nq, 65536, 64, 0, _lib.BF16, 1) == 1
-    assert sel(1, 32, 9, 65536, 64, 0, _lib.BF16, 1) == 0
-    assert sel(1, 32, 65, 65536, 128, 1, _lib.BF16, 3) == 0       # a second query tile
+    assert sel(1, 32, 65, 65536, 64, 0, _lib.BF16, 1) == 0        # a second query tile
+    assert sel(1, 32, 65, 65536, 128, 1, _lib.BF16, 3) == 0
     assert sel(1, 32, 64, 65536, 128, 1, _lib.F32, 3) == 0        # bf16 only
     assert sel(1, 32, 0, 65536, 128, 1, _lib.BF16, 3) == 0        # nothing to add
     # 1024 heads of 64 queries: 64 MiB of fp32 sums for both gradients, 32 MiB for one

@@ -96,6 +96,33 @@ def test_fused_backward_short_query_block_over_64k_keys():
             check_grad(to64(grads[n][0, hh]), ref[hh][n], q1.dtype, f"64x64K head {hh} {n}")
 
 
+def test_fused_backward_walks_several_key_blocks_per_workgroup_with_ragged_ends():
+    """With one query tile (N_Q <= 64) a workgroup walks several 128-key
+    blocks, the next block's keys copied while the current one is worked on.
+    3 heads x 514 key blocks take 3 blocks a workgroup: the last workgroup of
+    each head has one block left, and the last block 36 keys (N_K = 65,700).
+    Causal: the frontier crosses the last blocks.  All heads against the
+    oracle; dK reproduced bit for bit."""
+    B, H, NQ, NK, d = 1, 3, 40, 65700, 128
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.2, seed=27, device=DEV)
+    grads = compare(q1, k1, q2, k2, 1.0 / math.sqrt(d), True, tag="3x40x65700")
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, 1.0 / math.sqrt(d), True)
+    again = ops.streamkl_bwd_fused(q1, k1, q2, k2, kl, l1, l2, None, 1.0 / math.sqrt(d), True)
+    torch.cuda.synchronize()
+    assert torch.equal(grads["dk1"], again[1]) and torch.equal(grads["dk2"], again[3])
+
+
+@pytest.mark.parametrize("mask", [1, 2, 3])
+def test_fused_backward_several_key_blocks_d64_upstream_gradient(mask):
+    """The same walk at d = 64 with an upstream gradient and each gradient
+    selection: 2 heads x 514 key blocks (2 a workgroup), the last block one
+    key (N_K = 65,665), not causal."""
+    B, H, NQ, NK, d = 1, 2, 8, 65665, 64
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=28, device=DEV)
+    g = upstream_grad(B, H, NQ, seed=29, device=DEV)
+    compare(q1, k1, q2, k2, 0.125, False, g=g, mask=mask, tag=f"2x8x65665 mask {mask}")
+
+
 def test_fused_backward_identical_teacher_student_gives_zero_gradients():
     q, k, _, _ = make_inputs(1, 2, 70, 300, 128, torch.bfloat16, "iid", 0, seed=24, device=DEV)
     kl, l1, l2 = ops.streamkl_fwd(q, k, q, k, 0.1, True)

@@ -92,7 +92,8 @@ HALF_CASES = [
     (1, 2, 70, 3000, 64, True, 1, True, False),
     (1, 3, 1, 8192, 64, False, 3, True, True),      # decoding row
     (1, 2, 70, 3000, 128, False, 2, True, False),
-    (2, 2, 33, 5000, 64, True, 1, True, False),
+    (2, 2, 33, 5000, 64, True, 1, True, True),
+    (2, 2, 70, 5000, 64, True, 1, True, False),
     (2, 2, 33, 5000, 128, True, 1, True, True),
     (1, 32, 2048, 2048, 128, True, 3, False, False),
 ]
