@@ -247,6 +247,27 @@ def test_fwd_raised_shifts_with_exact_scores(dt, direction, causal):
     assert l1.abs().max() > 500      # the logits really are far from unit scale
 
 
+@pytest.mark.parametrize("shape", [(1, 16, 2048, 2048, 64), (2, 8, 1000, 1100, 128), (1, 24, 3000, 3000, 128),
+                                   (1, 17, 500, 500, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fwd_longest_first_order_covers_every_row(shape):
+    """The unsplit causal forward with fewer than 64 query blocks a head and
+    whole heads per XCD takes its blocks longest first over each XCD's heads
+    (2, 2, 3 and 2 heads per XCD here; the last grid, 34 workgroups, leaves
+    its last two outside the eight XCD ranges, and those keep the head-major
+    order).  Every row of every head against the oracle, so a workgroup that
+    computed another head's block, or none, shows."""
+    B, H, NQ, NK, d = shape
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.2, seed=NQ + H, device=DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, d ** -0.5, True, splits=1)
+    torch.cuda.synchronize()
+    ref = oracle_heads(q1, k1, q2, k2, d ** -0.5, True, range(B * H))
+    for hh in range(B * H):
+        b, h = divmod(hh, H)
+        for name, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
+            check_rows(to64(got[b, h]), ref[hh][name], q1.dtype, f"longest-first head {hh} {name}")
+
+
 def test_fwd_is_deterministic():
     q1, k1, q2, k2 = make_inputs(1, 4, 1024, 1024, 128, torch.bfloat16, "student", 0.2, seed=9, device=DEV)
     a = ops.streamkl_fwd(q1, k1, q2, k2, 0.09, True)
