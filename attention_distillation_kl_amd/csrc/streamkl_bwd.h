@@ -718,12 +718,16 @@ void bwd_kernel(BwdParams p) {
 
 // Sum of the key partitions' partial query gradients, in partition order
 // (deterministic), converted to the gradient's element type.  One thread per
-// four consecutive values of one row.
+// four consecutive values of one row; blockIdx.y picks the gradient, so both
+// requested gradients take one launch.
 template <bool BF16>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict__ part, int nsplit, size_t n4,
-                                                        char *out) {
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict__ part0, char *out0,
+                                                        const float *__restrict__ part1, char *out1, int nsplit,
+                                                        size_t n4) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
+  const float *part = blockIdx.y ? part1 : part0;
+  char *out = blockIdx.y ? out1 : out0;
   const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + i;
   f32x4 acc = src[0];
   for (int s = 1; s < nsplit; ++s) {
@@ -783,10 +787,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const size_t n4 = size_t(a.bh) * a.nq * D / 4;
   const size_t rblocks = (n4 + 255) / 256;
   if (rblocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
-  if (MASK & 1)
-    dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks)), dim3(256), 0, stream>>>(p.part1, p.nsplit, n4, p.dq1);
-  if (MASK & 2)
-    dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks)), dim3(256), 0, stream>>>(p.part2, p.nsplit, n4, p.dq2);
+  const int ngrad = ((MASK & 1) ? 1 : 0) + ((MASK & 2) ? 1 : 0);
+  const float *part0 = (MASK & 1) ? p.part1 : p.part2;
+  char *out0 = (MASK & 1) ? p.dq1 : p.dq2;
+  dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks), unsigned(ngrad)), dim3(256), 0, stream>>>(part0, out0, p.part2, p.dq2,
+                                                                                             p.nsplit, n4);
   return hipGetLastError();
 }
 

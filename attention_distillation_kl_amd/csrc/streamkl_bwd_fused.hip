@@ -607,10 +607,15 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4 *x, size_t n4) {
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256) x[i] = f32x4{};
 }
 
-// dq = f * ws, fp32 -> bf16 (nearest even); 4 values per thread.
-__global__ __launch_bounds__(256) void convert_kernel(const f32x4 *ws, size_t n4, float f, u32x2 *out) {
+// dq = f * ws, fp32 -> bf16 (nearest even); 4 values per thread.  blockIdx.y
+// picks the gradient, so both requested gradients take one launch.
+__global__ __launch_bounds__(256) void convert_kernel(const f32x4 *ws0, float f0, u32x2 *out0, const f32x4 *ws1,
+                                                      float f1, u32x2 *out1, size_t n4) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
+  const f32x4 *ws = blockIdx.y ? ws1 : ws0;
+  const float f = blockIdx.y ? f1 : f0;
+  u32x2 *out = blockIdx.y ? out1 : out0;
   const f32x4 v = ws[i];
   out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
 }
@@ -668,12 +673,12 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
   if (n4 > 0) {
     const size_t cb = (n4 + 255) / 256;
     if (cb > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
-    if (MASK & 1)
-      convert_kernel<<<dim3(unsigned(cb)), dim3(256), 0, stream>>>(reinterpret_cast<const f32x4 *>(p.ws1), n4,
-                                                                   a.scale * a.scale, static_cast<u32x2 *>(a.dq1));
-    if (MASK & 2)
-      convert_kernel<<<dim3(unsigned(cb)), dim3(256), 0, stream>>>(reinterpret_cast<const f32x4 *>(p.ws2), n4,
-                                                                   a.scale, static_cast<u32x2 *>(a.dq2));
+    // Gradient 0 of the launch is dq1 when requested, else dq2.
+    const f32x4 *w0 = reinterpret_cast<const f32x4 *>((MASK & 1) ? p.ws1 : p.ws2);
+    const float f0 = (MASK & 1) ? a.scale * a.scale : a.scale;
+    u32x2 *o0 = static_cast<u32x2 *>((MASK & 1) ? a.dq1 : a.dq2);
+    convert_kernel<<<dim3(unsigned(cb), unsigned(ngrad)), dim3(256), 0, stream>>>(
+        w0, f0, o0, reinterpret_cast<const f32x4 *>(p.ws2), a.scale, static_cast<u32x2 *>(a.dq2), n4);
   }
   return hipGetLastError();
 }
