@@ -112,6 +112,9 @@ struct BwdParams {
   // kernel sums the partitions in order and converts.
   int nsplit, tps;
   float *part1, *part2;
+  // Causal, unsplit: the stationary blocks' ranks are taken over each XCD's
+  // heads (longest_first) instead of head by head.
+  int lf;
 };
 
 // Per-row constants of the recompute.
@@ -205,12 +208,18 @@ void bwd_kernel(BwdParams p) {
   static_assert(!SPLIT || ROLE == ROLE_DQ, "key partitions are for the query-gradient role");
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_bh = SPLIT ? p.nsb * p.nsplit : p.nsb;
-  const int bh = bid / per_bh;
+  int bh = bid / per_bh;
   const int rem = bid - bh * per_bh;
   const int split = SPLIT ? rem / p.nsb : 0;
-  const int sbr = rem - split * p.nsb;
+  int sbr = rem - split * p.nsb;
   // Longest rows first: for causal problems the last query blocks (ROLE_DQ)
-  // and the first key blocks (ROLE_DK) see the most partners.
+  // and the first key blocks (ROLE_DK) see the most partners; with p.lf the
+  // ranks are taken over the XCD's heads (longest_first).
+  if (CAUSAL && !SPLIT && p.lf) {
+    const BlockPos bp = longest_first(bid, gridDim.x, p.nsb);
+    bh = bp.bh;
+    sbr = bp.rank;
+  }
   const int sblk = (CAUSAL && ROLE == ROLE_DQ) ? p.nsb - 1 - sbr : sbr;
 
   const int ns = ROLE == ROLE_DQ ? p.nq : p.nk;  // stationary rows per head
@@ -771,6 +780,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const size_t part_elems = size_t(a.bh) * a.nq * D * p.nsplit;  // per requested gradient
   p.part1 = split ? a.part : nullptr;
   p.part2 = split ? a.part + ((MASK & 1) ? part_elems : 0) : nullptr;
+  // Resident workgroups per XCD: 32 CUs x (4 SIMDs x waves per SIMD / waves).
+  constexpr long long kResidentPerXcd = 32LL * (4 * C::kWavesPerEU / C::kWaves);
+  p.lf = (CAUSAL && !split && longest_first_pays((long long)p.nsb * a.bh, p.nsb, kResidentPerXcd)) ? 1 : 0;
   const long long blocks = (long long)p.nsb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;

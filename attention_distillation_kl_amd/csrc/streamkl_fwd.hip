@@ -493,17 +493,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
 }
 
 // Whether the causal, unsplit forward takes its query blocks' ranks over each
-// XCD's heads (longest_first): where a head has fewer query blocks than an
-// XCD has resident workgroups (two per CU, 32 CUs) -- only then does taking
-// the heads one after the other leave long blocks for the end -- and each
-// XCD's share of the grid is whole heads.  Measured at 64 heads x 32 query
-// blocks: -11%; at 128 blocks a head, where it would not help, the shared L2
-// made it 2-4% slower.
-inline bool fwd_longest_first(long long nwg, long long nqb) {
-  constexpr long long kResidentPerXcd = 2 * 32;
-  const long long per = nwg / 8;
-  return nqb < kResidentPerXcd && per > 0 && per % nqb == 0;
-}
+// XCD's heads (longest_first_pays, with two resident workgroups per CU and 32
+// CUs per XCD).  Measured at 64 heads x 32 query blocks: -11%; at 128 blocks
+// a head, where it would not help, the shared L2 made it 2-4% slower.
+inline bool fwd_longest_first(long long nwg, long long nqb) { return longest_first_pays(nwg, nqb, 2 * 32); }
 
 template <bool BF16, int D, bool CAUSAL, bool RM = false>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {

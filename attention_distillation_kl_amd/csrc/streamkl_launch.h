@@ -29,6 +29,17 @@ struct BwdArgs {
   float *part = nullptr;   // their fp32 partial gradients (see bwd_dq_workspace_floats)
 };
 
+// Whether a causal grid of nwg workgroups, nblk a head, takes its blocks
+// longest first over each XCD's heads (longest_first in streamkl_device.h):
+// where a head has fewer blocks than an XCD holds resident workgroups --
+// only then does taking the heads one after the other leave long blocks for
+// the end of the grid -- and each XCD's share of the grid is whole heads.
+// Elsewhere that order only spreads more heads over each XCD's L2.
+inline bool longest_first_pays(long long nwg, long long nblk, long long resident_per_xcd) {
+  const long long per = nwg / 8;
+  return nblk < resident_per_xcd && per > 0 && per % nblk == 0;
+}
+
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // The library's choice of key partitions for a forward problem (1 = none).
 int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal);
