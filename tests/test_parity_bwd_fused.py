@@ -113,14 +113,17 @@ def test_fused_backward_walks_several_key_blocks_per_workgroup_with_ragged_ends(
 
 
 @pytest.mark.parametrize("mask", [1, 2, 3])
-def test_fused_backward_several_key_blocks_d64_upstream_gradient(mask):
-    """The same walk at d = 64 with an upstream gradient and each gradient
-    selection: 2 heads x 514 key blocks (2 a workgroup), the last block one
-    key (N_K = 65,665), not causal."""
-    B, H, NQ, NK, d = 1, 2, 8, 65665, 64
-    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=28, device=DEV)
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_backward_several_key_blocks_upstream_gradient(mask, d):
+    """The same walk with an upstream gradient and each gradient selection:
+    2 heads x 514 key blocks (2 a workgroup), the last block one key
+    (N_K = 65,665); at d = 64 8 queries, not causal, at d = 128 40 queries,
+    causal."""
+    B, H, NK = 1, 2, 65665
+    NQ, causal = (8, False) if d == 64 else (40, True)
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=28 + d, device=DEV)
     g = upstream_grad(B, H, NQ, seed=29, device=DEV)
-    compare(q1, k1, q2, k2, 0.125, False, g=g, mask=mask, tag=f"2x8x65665 mask {mask}")
+    compare(q1, k1, q2, k2, d ** -0.5, causal, g=g, mask=mask, tag=f"2x{NQ}x65665 d {d} mask {mask}")
 
 
 def test_fused_backward_identical_teacher_student_gives_zero_gradients():
