@@ -179,6 +179,16 @@ def test_default_split_choice(lib):
     # short query block over long keys: split; a grid that fills the GPU: not
     assert _lib.fwd_splits(1, 32, 2048, 65536, 128, 0, _lib.BF16) > 1
     assert _lib.fwd_splits(1, 32, 32768, 32768, 128, 1, _lib.BF16) == 1
+    # causal grids of more than one round whose heads fit the XCD ranges
+    # balance by order, unsplit (32 x 8K: 1024 workgroups of 32 blocks a
+    # head; 64 x 4K); within one round (32 x 4K, 16 x 8K: 512 workgroups)
+    # key partitions still balance them
+    assert _lib.fwd_splits(1, 32, 8192, 8192, 128, 1, _lib.BF16) == 1
+    assert _lib.fwd_splits(1, 64, 4096, 4096, 128, 1, _lib.BF16) == 1
+    assert _lib.fwd_splits(1, 32, 4096, 4096, 128, 1, _lib.BF16) == 4
+    assert _lib.fwd_splits(1, 16, 8192, 8192, 128, 1, _lib.BF16) == 4
+    # 12 heads x 8K: 384 workgroups, within one round
+    assert _lib.fwd_splits(1, 12, 8192, 8192, 128, 1, _lib.BF16) > 1
     assert _lib.fwd_splits(1, 1, 1, 64, 128, 0, _lib.BF16) == 1      # one key tile: nothing to split
     assert _lib.fwd_splits(0, 1, 1, 64, 128, 0, _lib.BF16) == 1      # invalid sizes
     for nq, nk in ((1, 65536), (1, 1 << 20), (64, 4096)):
