@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates HBM byte counters)")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip sampling the GPU clock under load after the timed steps")
+                    help="skip sampling the GPU clock under load after the timed steps (sampled only for steps of 20 ms and more)")
     ap.add_argument("--sweep", action="store_true",
                     help="context-length sweep instead of the headline: N = 4K..--sweep-max, "
                          "forward and each backward configuration, causal and not; one JSON line per N")
@@ -409,15 +409,25 @@ def main():
         roof["executed_tflops"] = round(ex / (kern[dom] * 1e-3) / 1e12, 2)
 
     # The graphics clock, sampled while untimed steps keep the GPU busy (the
-    # clock drops within milliseconds once the GPU idles).
+    # clock drops within milliseconds once the GPU idles, and takes a while to
+    # come back).  Steps are queued about 20 ms at a time and run for about
+    # 200 ms before the sample starts.  Only steps of 20 ms and more are
+    # sampled: steps made of shorter kernels leave XCDs idle between them,
+    # and the reading then swings between idle and load clocks.
     clock = None
-    if not args.no_clock:
+    if not args.no_clock and step_ms >= 20.0:
         import threading
         got = {}
+        per_sync = max(1, int(20.0 / max(step_ms, 1e-3)))
+        for _ in range(10):
+            for _ in range(per_sync):
+                step()
+            torch.cuda.synchronize()
         th = threading.Thread(target=lambda: got.update(c=sample_clock()))
         th.start()
         while th.is_alive():
-            step()
+            for _ in range(per_sync):
+                step()
             torch.cuda.synchronize()
         th.join()
         clock = got.get("c")
