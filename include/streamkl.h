@@ -98,8 +98,10 @@ streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2,
  * partition, and 1 (no split) when the unsplit grid already fills the GPU.
  * Causal problems with N_Q > N_K / 2, whose query blocks carry very
  * different amounts of work, get about four times as many workgroups (at
- * least 16 key tiles per partition) so that they balance.  Invalid sizes
- * give 1.
+ * least 16 key tiles per partition) so that they balance -- unless the
+ * unsplit grid spans more than one round of resident workgroups and the
+ * kernel can take its query blocks longest first over each XCD's heads,
+ * which balances it without partitions.  Invalid sizes give 1.
  */
 int streamkl_fwd_splits(int B, int H, int N_Q, int N_K, int d, int causal, int dtype);
 
