@@ -460,36 +460,86 @@ void fwd_kernel(FwdParams p) {
   }
 }
 
-// Split-K merge: one thread per row combines the partitions' states with the
-// rescale of the online update (empty partitions, m = -inf, weigh 0) and
-// finalises the row as the unsplit kernel does.  With one partition it
-// reproduces the unsplit results bit for bit.
+// Split-K merge.  A row's partition states are combined with the rescale of
+// the online update (empty partitions, m = -inf, weigh 0) and the row is then
+// finalised as the unsplit kernel does.  G = min(64, next power of two >=
+// nsplit) consecutive lanes take one row: lane j reads partitions j, j + G,
+// ..., so that a row's loads are in flight together rather than one
+// partition after another, and the lanes' states are then combined pairwise
+// across the group.  With one partition the row's state is finalised as
+// stored, which reproduces the unsplit results bit for bit.
+struct RowState {
+  float m1, m2, l1, l2, acc;
+};
+__device__ __forceinline__ RowState combine(const RowState &a, const RowState &b, float c) {
+  RowState r;
+  r.m1 = vmax(a.m1, b.m1);
+  r.m2 = vmax(a.m2, b.m2);
+  const float fa1 = (a.m1 == -INFINITY) ? 0.f : fast_exp2((a.m1 - r.m1) * c);
+  const float fb1 = (b.m1 == -INFINITY) ? 0.f : fast_exp2((b.m1 - r.m1) * c);
+  const float fa2 = (a.m2 == -INFINITY) ? 0.f : fast_exp2((a.m2 - r.m2) * c);
+  const float fb2 = (b.m2 == -INFINITY) ? 0.f : fast_exp2((b.m2 - r.m2) * c);
+  r.l1 = fmaf(a.l1, fa1, b.l1 * fb1);
+  r.l2 = fmaf(a.l2, fa2, b.l2 * fb2);
+  r.acc = fmaf(a.acc, fa1, b.acc * fb1);
+  return r;
+}
+
+template <int G>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part, int nsplit, size_t rows,
                                                     float scale, float c, float *kl, float *lse1, float *lse2) {
-  const size_t r = size_t(blockIdx.x) * 256 + threadIdx.x;
-  if (r >= rows) return;
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "a row's lanes lie in one wave");
+  const size_t t = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const size_t r = t / G;
+  const int j = int(t % G);
+  // No early exit: every lane of a group takes part in the exchanges below
+  // (a group is wholly inside or wholly past the last row).
+  const bool live = r < rows;
   const size_t stride = size_t(nsplit) * rows;
-  const float *st = part + r;
-  float M1 = -INFINITY, M2 = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) {
-    M1 = vmax(M1, st[ST_M1 * stride + size_t(s) * rows]);
-    M2 = vmax(M2, st[ST_M2 * stride + size_t(s) * rows]);
+  RowState s{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
+  if (live) {
+    for (int k = j; k < nsplit; k += G) {
+      const float *st = part + size_t(k) * rows + r;
+      const RowState x{st[ST_M1 * stride], st[ST_M2 * stride], st[ST_L1 * stride], st[ST_L2 * stride],
+                       st[ST_ACC * stride]};
+      s = (k == j) ? x : combine(s, x, c);
+    }
   }
-  float L1 = 0.f, L2 = 0.f, A = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t o = size_t(s) * rows;
-    const float m1 = st[ST_M1 * stride + o], m2 = st[ST_M2 * stride + o];
-    const float f1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - M1) * c);
-    const float f2 = (m2 == -INFINITY) ? 0.f : fast_exp2((m2 - M2) * c);
-    L1 = fmaf(st[ST_L1 * stride + o], f1, L1);
-    L2 = fmaf(st[ST_L2 * stride + o], f2, L2);
-    A = fmaf(st[ST_ACC * stride + o], f1, A);
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    const RowState y{__shfl_xor(s.m1, o), __shfl_xor(s.m2, o), __shfl_xor(s.l1, o), __shfl_xor(s.l2, o),
+                     __shfl_xor(s.acc, o)};
+    s = combine(s, y, c);
   }
-  const float l1 = M1 * scale + logf(L1);
-  const float l2 = M2 * scale + logf(L2);
-  kl[r] = scale * (A / L1) + l2 - l1;
-  lse1[r] = l1;
-  lse2[r] = l2;
+  if (live && j == 0) {
+    const float l1 = s.m1 * scale + logf(s.l1);
+    const float l2 = s.m2 * scale + logf(s.l2);
+    kl[r] = scale * (s.acc / s.l1) + l2 - l1;
+    lse1[r] = l1;
+    lse2[r] = l2;
+  }
+}
+
+// Launches the merge with the smallest lane group that holds nsplit
+// partitions (at most 64 lanes; more partitions are looped over).
+inline hipError_t launch_merge(const float *part, int nsplit, size_t rows, float scale, float c, float *kl,
+                               float *lse1, float *lse2, hipStream_t stream) {
+  int g = 1;
+  while (g < nsplit && g < 64) g *= 2;
+  const size_t threads = rows * size_t(g);
+  const size_t blocks = (threads + 255) / 256;
+  if (blocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
+  const dim3 grid{unsigned(blocks)}, block{256u};
+  switch (g) {
+    case 1: merge_kernel<1><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 2: merge_kernel<2><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 4: merge_kernel<4><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 8: merge_kernel<8><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 16: merge_kernel<16><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 32: merge_kernel<32><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    default: merge_kernel<64><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+  }
+  return hipGetLastError();
 }
 
 // Whether the causal, unsplit forward takes its query blocks' ranks over each
@@ -529,11 +579,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
                          : reinterpret_cast<const void *>(&fwd_kernel<BF16, D, CAUSAL, false, RM>);
   hipError_t e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, C::kLdsBytes, stream);
   if (e != hipSuccess || !split) return e;
-  const size_t mblocks = (p.rows + 255) / 256;
-  if (mblocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
-  merge_kernel<<<dim3(unsigned(mblocks)), dim3(256), 0, stream>>>(a.part, p.nsplit, p.rows, p.scale, p.c, a.kl,
-                                                                  a.lse1, a.lse2);
-  return hipGetLastError();
+  return launch_merge(a.part, p.nsplit, p.rows, p.scale, p.c, a.kl, a.lse1, a.lse2, stream);
 }
 
 }  // namespace
