@@ -46,6 +46,8 @@ CASES = [
     (1, 1, 257, 2048, 64, "bf16", True, 9),
     (1, 1, 5, 20, 128, "bf16", False, 2),      # under 32 keys: one wave of each pair scores none
     (1, 2, 20, 20, 128, "bf16", True, 3),      # the same, causal, with empty partitions
+    (1, 2, 40, 3000, 64, "bf16", True, 33),    # the merge's widest lane group, 31 lanes without a partition
+    (1, 2, 3, 5000, 128, "bf16", False, 1024), # the most partitions: lanes take several, 945 are empty
 ]
 
 
