@@ -135,9 +135,10 @@ int streamkl_bwd_fused_selected(int B, int H, int N_Q, int N_K, int d, int causa
   if (causal && N_Q > N_K) return 0;
   // Short query blocks only, where the fused form measured faster than the
   // two-kernel form: one 64-row query tile per head, which a workgroup keeps
-  // while it walks its key blocks (1.0-2.3x at d = 128 and d = 64; slower
-  // from 96 queries, with a second tile).  And the fp32 query-gradient
-  // buffer within L2, the page's criterion.
+  // while it walks its key blocks (1.2-2.5x at d = 128 and d = 64 from 8K
+  // keys per head; 0.76-1.6x, calls of 30-60 us, on small grids of 2K-16K
+  // keys; slower from 96 queries, with a second tile).  And the fp32
+  // query-gradient buffer within L2, the page's criterion.
   if (N_Q > 64) return 0;
   return streamkl::bwd_fused_workspace_floats(B * H, N_Q, d, grad_mask) * sizeof(float) <= kL2Bytes ? 1 : 0;
 }
