@@ -17,7 +17,7 @@ NOALLOC_SCRATCH_BYTES = 16 << 20   # STREAMKL_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splits", "streamkl_fwd_workspace_size", "streamkl_fwd_splitk",
            "streamkl_fwd_splitk_noalloc",
-           "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dq_ws", "streamkl_bwd_dk",
+           "streamkl_bwd", "streamkl_bwd_dq", "streamkl_bwd_dq_ws", "streamkl_bwd_dk", "streamkl_bwd_dk_ws",
            "streamkl_bwd_workspace_size", "streamkl_bwd_fused", "streamkl_bwd_fused_workspace_size",
            "streamkl_bwd_fused_selected", "streamkl_status_str", "streamkl_abi_version")
 
@@ -69,6 +69,8 @@ def load(path: str = None):
     lib.streamkl_bwd_dq_ws.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
                                        _f, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]
     lib.streamkl_bwd_dq_ws.restype = _i
+    lib.streamkl_bwd_dk_ws.argtypes = lib.streamkl_bwd_dq_ws.argtypes
+    lib.streamkl_bwd_dk_ws.restype = _i
     lib.streamkl_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
     lib.streamkl_bwd_workspace_size.restype = _sz
     lib.streamkl_bwd_fused.argtypes = lib.streamkl_bwd.argtypes
@@ -142,6 +144,13 @@ def bwd_dq_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causa
     """streamkl_bwd_dq_ws: the query-gradient half with the backward's workspace."""
     return load().streamkl_bwd_dq_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal,
                                      dtype, grad_mask, dq1, dq2, workspace, workspace_bytes, stream)
+
+
+def bwd_dk_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal, dtype, grad_mask,
+              dk1, dk2, workspace, workspace_bytes, stream):
+    """streamkl_bwd_dk_ws: the key-gradient half with the backward's workspace."""
+    return load().streamkl_bwd_dk_ws(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, NQ, NK, d, scale, causal,
+                                     dtype, grad_mask, dk1, dk2, workspace, workspace_bytes, stream)
 
 
 def bwd_workspace_size(B, H, NQ, NK, d, causal, dtype, grad_mask):

@@ -104,13 +104,22 @@ streamkl_status streamkl_fwd_splitk(const void *q1, const void *k1, const void *
 
 namespace {
 
+bool split_args_ok(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+  if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return false;
+  if ((dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) || grad_mask < 1 || grad_mask > 3) return false;
+  return (long long)B * H <= INT32_MAX;
+}
+
 // Key partitions of the query-gradient kernel for these arguments (1 = none).
 int bwd_dq_splits(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
-  if (B <= 0 || H <= 0 || N_Q <= 0 || N_K <= 0 || (d != 64 && d != 128)) return 1;
-  if ((dtype != STREAMKL_F32 && dtype != STREAMKL_BF16) || grad_mask < 1 || grad_mask > 3) return 1;
-  const long long bh = (long long)B * H;
-  if (bh > INT32_MAX) return 1;
-  return streamkl::bwd_dq_default_splits(int(bh), N_Q, N_K, d, dtype == STREAMKL_BF16, grad_mask);
+  if (!split_args_ok(B, H, N_Q, N_K, d, dtype, grad_mask)) return 1;
+  return streamkl::bwd_dq_default_splits(B * H, N_Q, N_K, d, dtype == STREAMKL_BF16, grad_mask);
+}
+
+// Query partitions of the key-gradient kernel for these arguments (1 = none).
+int bwd_dk_splits(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+  if (!split_args_ok(B, H, N_Q, N_K, d, dtype, grad_mask)) return 1;
+  return streamkl::bwd_dk_default_splits(B * H, N_Q, N_K, d, dtype == STREAMKL_BF16, grad_mask);
 }
 
 }  // namespace
@@ -118,10 +127,25 @@ int bwd_dq_splits(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mas
 namespace {
 
 // Workspace of the query-gradient half with key partitions (0 without).
-size_t partitioned_ws_bytes(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+size_t dq_ws_bytes(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
   const int s = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
   if (s <= 1) return 0;
   return streamkl::bwd_dq_workspace_floats(B * H, N_Q, d, grad_mask, s) * sizeof(float);
+}
+
+// Workspace of the key-gradient half with query partitions (0 without).
+size_t dk_ws_bytes(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+  const int s = bwd_dk_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
+  if (s <= 1) return 0;
+  return streamkl::bwd_dk_workspace_floats(B * H, N_K, d, grad_mask, s) * sizeof(float);
+}
+
+// The two-kernel form's workspace: the halves run one after the other on one
+// stream and share it.
+size_t partitioned_ws_bytes(int B, int H, int N_Q, int N_K, int d, int dtype, int grad_mask) {
+  const size_t q = dq_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask);
+  const size_t k = dk_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask);
+  return q > k ? q : k;
 }
 
 // Combined L2 of the eight XCDs (4 MiB each).
@@ -180,18 +204,19 @@ streamkl_status prepare_bwd(const void *q1, const void *k1, const void *q2, cons
 
 bool bwd_is_noop(int B, int H, int N_Q, int N_K) { return (long long)B * H == 0 || (N_Q == 0 && N_K == 0); }
 
-// Checks the caller's workspace against streamkl_bwd_workspace_size and, where
-// that size is not zero (short query blocks), switches the query-gradient
-// kernel to key partitions whose partial sums go to the workspace.
-streamkl_status attach_dq_workspace(streamkl::BwdArgs &a, int B, int H, int N_Q, int N_K, int d, int causal,
-                                    int dtype, int grad_mask, void *workspace, size_t workspace_bytes) {
-  (void)causal;
-  const size_t need = partitioned_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask);
+// Checks the caller's workspace against what the requested halves need (dq:
+// the query-gradient kernel's key partitions, dk: the key-gradient kernel's
+// query partitions) and switches each half that has partitions to them, with
+// their partial sums in the workspace.
+streamkl_status attach_workspace(streamkl::BwdArgs &a, int B, int H, int N_Q, int N_K, int d, int dtype,
+                                 int grad_mask, void *workspace, size_t workspace_bytes, bool dq, bool dk) {
+  const size_t nq = dq ? dq_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask) : 0;
+  const size_t nk = dk ? dk_ws_bytes(B, H, N_Q, N_K, d, dtype, grad_mask) : 0;
+  const size_t need = nq > nk ? nq : nk;
   if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace)))) return STREAMKL_ERR_WORKSPACE;
-  if (need > 0) {
-    a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
-    a.part = static_cast<float *>(workspace);
-  }
+  if (need > 0) a.part = static_cast<float *>(workspace);
+  if (nq > 0) a.dq_splits = bwd_dq_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
+  if (nk > 0) a.dk_splits = bwd_dk_splits(B, H, N_Q, N_K, d, dtype, grad_mask);
   return STREAMKL_OK;
 }
 
@@ -209,7 +234,7 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2, con
   streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
                                   dtype, grad_mask, dq1, dk1, dq2, dk2, true, true, a);
   if (s != STREAMKL_OK) return s;
-  s = attach_dq_workspace(a, B, H, N_Q, N_K, d, causal, dtype, grad_mask, workspace, workspace_bytes);
+  s = attach_workspace(a, B, H, N_Q, N_K, d, dtype, grad_mask, workspace, workspace_bytes, true, true);
   if (s != STREAMKL_OK) return s;
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -241,10 +266,26 @@ streamkl_status streamkl_bwd_dq_ws(const void *q1, const void *k1, const void *q
   streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
                                   dtype, grad_mask, dq1, nullptr, dq2, nullptr, true, false, a);
   if (s != STREAMKL_OK) return s;
-  s = attach_dq_workspace(a, B, H, N_Q, N_K, d, causal, dtype, grad_mask, workspace, workspace_bytes);
+  s = attach_workspace(a, B, H, N_Q, N_K, d, dtype, grad_mask, workspace, workspace_bytes, true, false);
   if (s != STREAMKL_OK) return s;
   if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
   return streamkl::launch_bwd_dq(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
+                                                                                     : STREAMKL_ERR_HIP;
+}
+
+streamkl_status streamkl_bwd_dk_ws(const void *q1, const void *k1, const void *q2, const void *k2,
+                                   const float *kl, const float *lse1, const float *lse2, const float *dkl,
+                                   int B, int H, int N_Q, int N_K, int d, float scale, int causal, int dtype,
+                                   int grad_mask, void *dk1, void *dk2, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  streamkl::BwdArgs a;
+  streamkl_status s = prepare_bwd(q1, k1, q2, k2, kl, lse1, lse2, dkl, B, H, N_Q, N_K, d, scale, causal,
+                                  dtype, grad_mask, nullptr, dk1, nullptr, dk2, false, true, a);
+  if (s != STREAMKL_OK) return s;
+  s = attach_workspace(a, B, H, N_Q, N_K, d, dtype, grad_mask, workspace, workspace_bytes, false, true);
+  if (s != STREAMKL_OK) return s;
+  if (bwd_is_noop(B, H, N_Q, N_K)) return STREAMKL_OK;
+  return streamkl::launch_bwd_dk(a, static_cast<hipStream_t>(stream)) == hipSuccess ? STREAMKL_OK
                                                                                      : STREAMKL_ERR_HIP;
 }
 

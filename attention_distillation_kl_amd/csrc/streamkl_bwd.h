@@ -25,8 +25,9 @@
 //            from its causal frontier to N_Q; it accumulates dK.
 // Both recompute S1, S2; neither needs atomics, and results are bitwise
 // deterministic.  For short query blocks the query-gradient role can also run
-// by key partitions (SPLIT below): partial sums in a caller's workspace, added
-// in a fixed order by dq_reduce_kernel.
+// by key partitions, and the key-gradient role of small grids with long
+// query streams by query partitions (SPLIT below): partial sums in a caller's
+// workspace, added in a fixed order by part_reduce_kernel.
 //
 // Per 32-row block of a streamed tile, each wave:
 //   1. S_t^T block (32 streamed x 32 stationary) = Y_t X_t^T with the
@@ -106,10 +107,14 @@ struct BwdParams {
   int nq, nk, nsb;    // nsb: stationary blocks per head
   float scale, c;     // c = scale * log2(e)
   float inv_scale;
-  // Key partitions of the query-gradient role (1 = none).  With nsplit > 1,
-  // partition s streams key tiles [s*tps, (s+1)*tps) and writes its fp32
-  // partial dQ_t (already scaled) to part_t[s][bh * N_Q + i][d]; a second
-  // kernel sums the partitions in order and converts.
+  // Partitions of the streamed rows (1 = none).  With nsplit > 1 the
+  // query-gradient role's partition s streams key tiles [s*tps, (s+1)*tps);
+  // the key-gradient role's splits the workgroup's own query range (from its
+  // causal frontier to N_Q) into nsplit runs of equal length, so that every
+  // key block's partitions are about equally long.  Each writes its fp32
+  // partial gradient (already scaled) to part_t[s][bh * rows + i][d], rows
+  // the role's stationary rows per head; a second kernel sums the
+  // partitions in order and converts.
   int nsplit, tps;
   float *part1, *part2;
   // Causal, unsplit: the stationary blocks' ranks are taken over each XCD's
@@ -169,8 +174,8 @@ inline bool bwd_dk_paired(int bh, int nq, int nk, bool bf16) {
   return unpaired < 2 * 256 || nq < 8192;
 }
 
-// SPLIT (query-gradient role only): the workgroup folds one key partition and
-// stores fp32 partial gradients instead of the gradients themselves.
+// SPLIT: the workgroup folds one partition of its streamed rows and stores
+// fp32 partial gradients instead of the gradients themselves.
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool SPLIT, bool PO>
 __global__ __attribute__((amdgpu_flat_work_group_size(BwdCfgOf<BF16, D, MASK, ROLE, PO>::kThreads,
                                                       BwdCfgOf<BF16, D, MASK, ROLE, PO>::kThreads),
@@ -205,7 +210,6 @@ void bwd_kernel(BwdParams p) {
 
   // With key partitions, the stationary blocks of one (head, partition) are
   // consecutive, so they share the partition's tiles in one L2.
-  static_assert(!SPLIT || ROLE == ROLE_DQ, "key partitions are for the query-gradient role");
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_bh = SPLIT ? p.nsb * p.nsplit : p.nsb;
   int bh = bid / per_bh;
@@ -283,8 +287,14 @@ void bwd_kernel(BwdParams p) {
   int tile0 = t_begin / C::kBT;
   int tile1 = (t_end + C::kBT - 1) / C::kBT;
   if (SPLIT) {  // this partition's share of the tiles
-    tile0 = max(tile0, split * p.tps);
-    tile1 = min(tile1, (split + 1) * p.tps);
+    if (ROLE == ROLE_DQ) {
+      tile0 = max(tile0, split * p.tps);
+      tile1 = min(tile1, (split + 1) * p.tps);
+    } else if (tile1 > tile0) {
+      const int len = (tile1 - tile0 + p.nsplit - 1) / p.nsplit;
+      tile0 += split * len;
+      tile1 = min(tile1, tile0 + len);
+    }
   }
   // ROLE_DQ: last admissible key; ROLE_DK: first admissible query.
   const int lim = ROLE == ROLE_DQ ? (CAUSAL ? min(srow + off, p.nk - 1) : p.nk - 1)
@@ -703,7 +713,7 @@ void bwd_kernel(BwdParams p) {
     };
     // A key partition's share: scaled fp32 partial sums, d values per row.
     auto store_part = [&](float *P, float f, const f32x16 (&A)[kMB]) {
-      float *row = P + (size_t(split) * (size_t(gridDim.x / per_bh) * p.nq) + size_t(bh) * p.nq + srow) * D;
+      float *row = P + (size_t(split) * (size_t(gridDim.x / per_bh) * ns) + size_t(bh) * ns + srow) * D;
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -714,7 +724,8 @@ void bwd_kernel(BwdParams p) {
         }
     };
     if constexpr (kPair) {
-      store(half ? O2 : O1, half ? f2 : f1, acc1);
+      if (SPLIT) store_part(half ? p.part2 : p.part1, half ? f2 : f1, acc1);
+      else store(half ? O2 : O1, half ? f2 : f1, acc1);
     } else if (SPLIT) {
       if (kG1) store_part(p.part1, f1, acc1);
       if (kG2) store_part(p.part2, f2, acc2);
@@ -725,12 +736,13 @@ void bwd_kernel(BwdParams p) {
   }
 }
 
-// Sum of the key partitions' partial query gradients, in partition order
-// (deterministic), converted to the gradient's element type.  One thread per
-// four consecutive values of one row; blockIdx.y picks the gradient, so both
-// requested gradients take one launch.
-template <bool BF16>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict__ part0, char *out0,
+// Sum of the partitions' partial gradients of one role (ROLE: the query
+// gradients' key partitions or the key gradients' query partitions), in
+// partition order (deterministic), converted to the gradient's element type.
+// One thread per four consecutive values of one row; blockIdx.y picks the
+// gradient, so both requested gradients take one launch.
+template <bool BF16, int ROLE>
+__global__ __launch_bounds__(256) void part_reduce_kernel(const float *__restrict__ part0, char *out0,
                                                         const float *__restrict__ part1, char *out1, int nsplit,
                                                         size_t n4) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
@@ -752,7 +764,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const float *__restrict_
 
 template <bool BF16, int D, bool CAUSAL, int ROLE, int MASK, bool GSIGN, bool PO>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
-  constexpr bool kCanSplit = ROLE == ROLE_DQ;
+  constexpr bool kCanSplit = true;
   using C = BwdCfgOf<BF16, D, MASK, ROLE, PO>;
   BwdParams p;
   p.q1 = static_cast<const char *>(a.q1);
@@ -774,10 +786,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
   p.inv_scale = float(1.0 / double(a.scale));
-  const bool split = kCanSplit && a.dq_splits > 1;
-  p.nsplit = split ? a.dq_splits : 1;
-  p.tps = (((a.nk + C::kBT - 1) / C::kBT) + p.nsplit - 1) / p.nsplit;
-  const size_t part_elems = size_t(a.bh) * a.nq * D * p.nsplit;  // per requested gradient
+  const int splits = ROLE == ROLE_DQ ? a.dq_splits : a.dk_splits;
+  const bool split = kCanSplit && splits > 1 && a.part != nullptr;
+  p.nsplit = split ? splits : 1;
+  p.tps = (((a.nk + C::kBT - 1) / C::kBT) + p.nsplit - 1) / p.nsplit;  // the query-gradient role's
+  const size_t part_elems = size_t(a.bh) * ns * D * p.nsplit;  // per requested gradient
   p.part1 = split ? a.part : nullptr;
   p.part2 = split ? a.part + ((MASK & 1) ? part_elems : 0) : nullptr;
   // Resident workgroups per XCD: 32 CUs x (4 SIMDs x waves per SIMD / waves).
@@ -796,14 +809,16 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   }
   hipError_t e = hipLaunchKernel(fn, dim3(unsigned(blocks)), dim3(C::kThreads), args, dyn, stream);
   if (e != hipSuccess || !split) return e;
-  const size_t n4 = size_t(a.bh) * a.nq * D / 4;
+  const size_t n4 = size_t(a.bh) * ns * D / 4;
   const size_t rblocks = (n4 + 255) / 256;
   if (rblocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
   const int ngrad = ((MASK & 1) ? 1 : 0) + ((MASK & 2) ? 1 : 0);
+  char *o1 = ROLE == ROLE_DQ ? p.dq1 : p.dk1;
+  char *o2 = ROLE == ROLE_DQ ? p.dq2 : p.dk2;
   const float *part0 = (MASK & 1) ? p.part1 : p.part2;
-  char *out0 = (MASK & 1) ? p.dq1 : p.dq2;
-  dq_reduce_kernel<BF16><<<dim3(unsigned(rblocks), unsigned(ngrad)), dim3(256), 0, stream>>>(part0, out0, p.part2, p.dq2,
-                                                                                             p.nsplit, n4);
+  char *out0 = (MASK & 1) ? o1 : o2;
+  part_reduce_kernel<BF16, ROLE><<<dim3(unsigned(rblocks), unsigned(ngrad)), dim3(256), 0, stream>>>(
+      part0, out0, p.part2, o2, p.nsplit, n4);
   return hipGetLastError();
 }
 

@@ -26,7 +26,12 @@ struct BwdArgs {
   bool causal, bf16;
   int grad_mask;  // 1: dq1/dk1, 2: dq2/dk2, 3: both
   int dq_splits = 1;       // key partitions of the query-gradient kernel when > 1
-  float *part = nullptr;   // their fp32 partial gradients (see bwd_dq_workspace_floats)
+  int dk_splits = 1;       // query partitions of the key-gradient kernel when > 1
+  // The partitions' fp32 partial gradients (bwd_dq_workspace_floats,
+  // bwd_dk_workspace_floats).  The key-gradient kernel and its reduction run
+  // before the query-gradient kernel on the same stream, so the two roles
+  // can share one workspace.
+  float *part = nullptr;
 };
 
 // Whether a causal grid of nwg workgroups, nblk a head, takes its blocks
@@ -49,6 +54,10 @@ int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal);
 int bwd_dq_default_splits(int bh, int nq, int nk, int d, bool bf16, int grad_mask);
 size_t bwd_dq_workspace_floats(int bh, int nq, int d, int grad_mask, int splits);
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t stream);
+// The same for the key-gradient kernel's query partitions (splits * bh * nk
+// * d floats per requested gradient).
+int bwd_dk_default_splits(int bh, int nq, int nk, int d, bool bf16, int grad_mask);
+size_t bwd_dk_workspace_floats(int bh, int nk, int d, int grad_mask, int splits);
 hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
 // The single-pass backward (bf16 only): dK in registers, dQ added with
 // atomics into `ws` (fp32, bwd_fused_workspace_floats values: the query

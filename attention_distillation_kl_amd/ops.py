@@ -142,7 +142,8 @@ def streamkl_bwd_fused(q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=None, cau
 
 def streamkl_bwd_workspace(q1, k1, causal=False, grad_mask=_lib.GRAD_ALL):
     """The backward's workspace for these sizes (a uint8 device tensor), or
-    None where the library needs none (query-gradient grids that fill the GPU)."""
+    None where the library needs none (query- and key-gradient grids that
+    fill the GPU)."""
     B, H, NQ, d = q1.shape
     n = _lib.bwd_workspace_size(B, H, NQ, k1.shape[2], d, int(bool(causal)), _dtype_code(q1), int(grad_mask))
     return torch.empty(n, device=q1.device, dtype=torch.uint8) if n else None
@@ -152,16 +153,15 @@ def streamkl_bwd_half(which, q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=Non
                      grad_mask=_lib.GRAD_ALL, out=None, workspace=None):
     """One half of the backward: which='dq' -> (dq1, dq2), 'dk' -> (dk1, dk2).
     ``out`` may supply preallocated output tensors (a pair, None for unrequested).
-    ``workspace`` (query half only; see streamkl_bwd_workspace) selects
-    streamkl_bwd_dq_ws, which partitions the keys for short query blocks as
-    streamkl_bwd does; without it the query half never partitions."""
+    ``workspace`` (see streamkl_bwd_workspace) selects streamkl_bwd_dq_ws or
+    streamkl_bwd_dk_ws, which partition the streamed rows where streamkl_bwd
+    does (the keys of short query blocks, the queries of small key grids);
+    without it neither half partitions."""
     B, H, NQ, NK, d = _check_inputs(q1, k1, q2, k2)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q1.device
     if which not in ("dq", "dk"):
         raise ValueError(f"which must be 'dq' or 'dk', not {which!r}")
-    if workspace is not None and which != "dq":
-        raise ValueError("only the query-gradient half takes a workspace")
     if dkl is not None:
         dkl = dkl.to(device=dev, dtype=torch.float32).expand(B, H, NQ).contiguous()
     like = (q1, q2) if which == "dq" else (k1, k2)
@@ -171,12 +171,13 @@ def streamkl_bwd_half(which, q1, k1, q2, k2, kl, lse1, lse2, dkl=None, scale=Non
     if workspace is not None:
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError(f"workspace must be a contiguous tensor on {dev}")
-        st = _lib.bwd_dq_ws(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1), _ptr(lse2),
-                            _ptr(dkl), B, H, NQ, NK, d, scale, int(bool(causal)), _dtype_code(q1),
-                            int(grad_mask), _ptr(out[0]), _ptr(out[1]), _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream(dev))
+        fn = _lib.bwd_dq_ws if which == "dq" else _lib.bwd_dk_ws
+        st = fn(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1), _ptr(lse2),
+                _ptr(dkl), B, H, NQ, NK, d, scale, int(bool(causal)), _dtype_code(q1),
+                int(grad_mask), _ptr(out[0]), _ptr(out[1]), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(dev))
         if st != _lib.OK:
-            raise _lib.StreamKLError(st, "streamkl_bwd_dq_ws")
+            raise _lib.StreamKLError(st, f"streamkl_bwd_{which}_ws")
         return out
     st = _lib.bwd_half(which, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1), _ptr(lse2),
                        _ptr(dkl), B, H, NQ, NK, d, scale, int(bool(causal)), _dtype_code(q1),

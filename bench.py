@@ -343,7 +343,8 @@ def main():
             if ev is not None:
                 ev[2].record()
         elif do_bwd:
-            ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dk)
+            ops.streamkl_bwd_half("dk", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dk,
+                                  workspace=ws)
             if ev is not None:
                 ev[2].record()
             ops.streamkl_bwd_half("dq", q1, k1, q2, k2, kl_, l1_, l2_, None, w.scale, w.causal, out=dq,

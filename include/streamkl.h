@@ -176,16 +176,20 @@ streamkl_status streamkl_fwd_splitk_noalloc(const void *q1, const void *k1,
 
 /*
  * streamkl_bwd_workspace_size -- bytes of device workspace streamkl_bwd needs
- * for these arguments.  0 whenever the query-gradient grid already fills the
- * GPU.  For short query blocks (few query-row workgroups per head) the query
- * gradients are computed by key partitions, like the split-K forward: each
- * (query block, partition) workgroup stores its fp32 partial dq_t and a
- * second kernel adds the partitions in a fixed order (deterministic, no
- * atomics); the workspace then holds splits * B*H*N_Q*d floats per requested
- * gradient, splits being the library's choice for these sizes.  Where
- * streamkl_bwd_fused_selected is 1 it is the larger of that and
- * streamkl_bwd_fused_workspace_size, so one workspace serves streamkl_bwd
- * and streamkl_bwd_dq_ws alike.
+ * for these arguments.  0 whenever the query-gradient and key-gradient grids
+ * already fill the GPU.  For short query blocks (few query-row workgroups
+ * per head) the query gradients are computed by key partitions, like the
+ * split-K forward: each (query block, partition) workgroup stores its fp32
+ * partial dq_t and a second kernel adds the partitions in a fixed order
+ * (deterministic, no atomics); splits * B*H*N_Q*d floats per requested
+ * gradient.  For small key grids with long query streams (few key-row
+ * workgroups, each streaming many query tiles) the key gradients are
+ * computed the same way by query partitions: splits * B*H*N_K*d floats per
+ * requested gradient.  splits is the library's choice for these sizes; the
+ * two halves run one after the other and share the workspace, whose size is
+ * the larger of the two.  Where streamkl_bwd_fused_selected is 1 it is the
+ * larger of that and streamkl_bwd_fused_workspace_size, so one workspace
+ * serves streamkl_bwd, streamkl_bwd_dq_ws and streamkl_bwd_dk_ws alike.
  */
 size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
                                    int causal, int dtype, int grad_mask);
@@ -209,7 +213,7 @@ size_t streamkl_bwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
  * With N_Q == 0 the key gradients are written as zeros.
  * Form: where streamkl_bwd_fused_selected(...) is 1 (bf16, short query
  * blocks, query-gradient buffer within L2) this is streamkl_bwd_fused;
- * otherwise the two-kernel form, streamkl_bwd_dk then streamkl_bwd_dq_ws,
+ * otherwise the two-kernel form, streamkl_bwd_dk_ws then streamkl_bwd_dq_ws,
  * whose results are bitwise reproducible.
  */
 streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
@@ -226,20 +230,24 @@ streamkl_status streamkl_bwd(const void *q1, const void *k1, const void *q2,
  * callers that schedule them separately (e.g. on two streams).  Same
  * arguments, meaning and errors as streamkl_bwd, restricted to the query
  * gradients (dq1, dq2) or to the key gradients (dk1, dk2).  Neither takes a
- * workspace: streamkl_bwd_dq never partitions the keys.  The page describes
+ * workspace: streamkl_bwd_dq never partitions the keys, nor streamkl_bwd_dk
+ * the queries.  The page describes
  * this split as the fallback of its fused backward when atomic contention on
  * dQ is high ("Strategia di Ricalcolo", kernel fusion bullet).
  *
- * streamkl_bwd_dq_ws -- the query-gradient half with streamkl_bwd's
- * workspace: workspace / workspace_bytes as for streamkl_bwd (at least
- * streamkl_bwd_workspace_size(...) bytes for the same sizes and grad_mask,
- * 16-byte aligned, caller-owned, STREAMKL_ERR_WORKSPACE otherwise).  Where
- * that size is not zero (short query blocks) the query gradients are
- * computed by key partitions, partial sums in the workspace, added in a
- * fixed order; otherwise it is streamkl_bwd_dq.  Where the fused form is
- * not selected, streamkl_bwd is streamkl_bwd_dk followed by
- * streamkl_bwd_dq_ws on one stream, with bitwise the same results; where it
- * is, the two halves remain a deterministic alternative to it.
+ * streamkl_bwd_dq_ws / streamkl_bwd_dk_ws -- the two halves with
+ * streamkl_bwd's workspace: workspace / workspace_bytes as for streamkl_bwd
+ * (at least streamkl_bwd_workspace_size(...) bytes for the same sizes and
+ * grad_mask, 16-byte aligned, caller-owned, STREAMKL_ERR_WORKSPACE
+ * otherwise).  Where the library partitions that half's streamed rows (the
+ * keys of short query blocks, the queries of small key grids with long
+ * query streams) the gradients are computed by partitions, partial sums in
+ * the workspace, added in a fixed order; otherwise they are streamkl_bwd_dq
+ * and streamkl_bwd_dk.  The two halves must not run at the same time on one
+ * workspace.  Where the fused form is not selected, streamkl_bwd is
+ * streamkl_bwd_dk_ws followed by streamkl_bwd_dq_ws on one stream, with
+ * bitwise the same results; where it is, the two halves remain a
+ * deterministic alternative to it.
  */
 streamkl_status streamkl_bwd_dq(const void *q1, const void *k1, const void *q2,
                                 const void *k2, const float *kl,
@@ -263,6 +271,14 @@ streamkl_status streamkl_bwd_dk(const void *q1, const void *k1, const void *q2,
                                 int N_K, int d, float scale, int causal,
                                 int dtype, int grad_mask, void *dk1, void *dk2,
                                 void *stream);
+streamkl_status streamkl_bwd_dk_ws(const void *q1, const void *k1,
+                                   const void *q2, const void *k2,
+                                   const float *kl, const float *lse1,
+                                   const float *lse2, const float *dkl, int B,
+                                   int H, int N_Q, int N_K, int d, float scale,
+                                   int causal, int dtype, int grad_mask,
+                                   void *dk1, void *dk2, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * streamkl_bwd_fused_workspace_size -- bytes of device workspace
