@@ -118,7 +118,8 @@ struct BwdParams {
   int nsplit, tps;
   float *part1, *part2;
   // Causal, unsplit: the stationary blocks' ranks are taken over each XCD's
-  // heads (longest_first) instead of head by head.
+  // heads (lf 1, longest_first) or over the whole grid (lf 2, rank_major)
+  // instead of head by head (0).
   int lf;
 };
 
@@ -218,9 +219,11 @@ void bwd_kernel(BwdParams p) {
   int sbr = rem - split * p.nsb;
   // Longest rows first: for causal problems the last query blocks (ROLE_DQ)
   // and the first key blocks (ROLE_DK) see the most partners; with p.lf the
-  // ranks are taken over the XCD's heads (longest_first).
+  // ranks are taken over the XCD's heads (longest_first) or over the whole
+  // grid (rank_major).
   if (CAUSAL && !SPLIT && p.lf) {
-    const BlockPos bp = longest_first(bid, gridDim.x, p.nsb);
+    const BlockPos bp = p.lf == 1 ? longest_first(bid, gridDim.x, p.nsb)
+                                  : rank_major(blockIdx.x, gridDim.x / p.nsb);
     bh = bp.bh;
     sbr = bp.rank;
   }
@@ -795,7 +798,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   p.part2 = split ? a.part + ((MASK & 1) ? part_elems : 0) : nullptr;
   // Resident workgroups per XCD: 32 CUs x (4 SIMDs x waves per SIMD / waves).
   constexpr long long kResidentPerXcd = 32LL * (4 * C::kWavesPerEU / C::kWaves);
-  p.lf = (CAUSAL && !split && longest_first_pays((long long)p.nsb * a.bh, p.nsb, kResidentPerXcd)) ? 1 : 0;
+  const long long nwg_all = (long long)p.nsb * a.bh;
+  p.lf = (!CAUSAL || split) ? 0
+         : longest_first_pays(nwg_all, p.nsb, kResidentPerXcd) ? 1
+         : rank_major_pays(nwg_all, p.nsb, kResidentPerXcd)    ? 2
+                                                                : 0;
   const long long blocks = (long long)p.nsb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;

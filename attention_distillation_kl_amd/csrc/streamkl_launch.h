@@ -45,6 +45,15 @@ inline bool longest_first_pays(long long nwg, long long nblk, long long resident
   return nblk < resident_per_xcd && per > 0 && per % nblk == 0;
 }
 
+// Whether a causal grid takes the rank-major order (rank_major in
+// streamkl_device.h) instead: more than one round of workgroups, and XCD
+// shares that are not whole heads, so that head by head one XCD would get a
+// head's long blocks and another its short ones.
+inline bool rank_major_pays(long long nwg, long long nblk, long long resident_per_xcd) {
+  const long long per = nwg / 8;
+  return nwg > 8 * resident_per_xcd && nblk > 0 && (nwg % 8 != 0 || per % nblk != 0);
+}
+
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 // The library's choice of key partitions for a forward problem (1 = none).
 int fwd_default_splits(int bh, int nq, int nk, int d, bool bf16, bool causal);

@@ -119,15 +119,18 @@ def test_bwd_single_configuration_masks_on_a_large_grid():
         check_grad(to64(full[n][0, hh]), ref[n], q1.dtype, f"16x8192 head {hh} {n}")
 
 
-@pytest.mark.parametrize("shape", [(1, 16, 2048, 2048, 128, True), (1, 32, 4096, 4096, 64, False)],
+@pytest.mark.parametrize("shape", [(1, 16, 2048, 2048, 128, True), (1, 32, 4096, 4096, 64, False),
+                                   (1, 36, 2048, 2048, 64, False)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_bwd_longest_first_order_covers_every_head(shape):
-    """Causal grids whose backward kernels take their blocks longest first
-    over each XCD's heads: 16 heads x 2K tokens for the paired key-gradient
+    """Causal grids whose backward kernels take their blocks longest first:
+    over each XCD's heads for 16 heads x 2K tokens in the paired key-gradient
     kernel (32 blocks a head, 64 resident per XCD; its query gradients go by
-    key partitions), 32 heads x 4K tokens for the query-gradient kernel (16
-    blocks a head, 32 resident, not partitioned).  All four gradients of
-    every head against the oracle."""
+    key partitions) and 32 heads x 4K tokens in the query-gradient kernel (16
+    blocks a head, 32 resident, not partitioned); over the whole grid (rank
+    major) for 36 heads x 2K tokens in both kernels (more than one round, and
+    4.5 heads per XCD).  All four gradients of every head against the
+    oracle."""
     B, H, NQ, NK, d, dq_partitioned = shape
     assert (_lib.bwd_workspace_size(B, H, NQ, NK, d, 1, _lib.BF16, 3) > 0) == dq_partitioned
     q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.2, seed=H + d, device=DEV)
