@@ -69,11 +69,14 @@ struct FwdParams {
   float *kl, *lse1, *lse2;
   int nq, nk, nqb;
   float scale, c;  // c = scale * log2(e)
-  // Split-K: the key tiles are dealt to nsplit partitions of tps tiles each;
-  // partition states go to part = [5][nsplit][bh * nq] (m1, m2, l1, l2, acc).
+  // Split-K: the key tiles are dealt to nsplit partitions of tps tiles each
+  // (causal grids in the rank-major order: each query block's own admissible
+  // tiles, in nsplit runs of equal length); partition states go to part =
+  // [5][nsplit][bh * nq] (m1, m2, l1, l2, acc).
   int nsplit, tps;
-  // Causal, unsplit: the query blocks' ranks are taken over each XCD's heads
-  // (longest_first) instead of head by head.
+  // Causal: the query blocks' ranks are taken over each XCD's heads (lf 1,
+  // unsplit, longest_first) or over the whole grid (lf 2, with partitions)
+  // instead of head by head (0).
   int lf;
   size_t rows;  // B * H * N_Q
   float *part;
@@ -103,15 +106,26 @@ void fwd_kernel(FwdParams p) {
 
   // Heads are contiguous in logical order (one head per XCD at a time); for
   // causal problems the longest query blocks of a head go first, or, with
-  // p.lf, the longest of all the XCD's heads (longest_first).
+  // p.lf, the longest of all the XCD's heads (longest_first) or of the whole
+  // grid (rank-major, causal grids with partitions).
   // With split-K, the query blocks of one (head, partition) are consecutive,
   // so they share the partition's K tiles in one L2.
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int per_bh = p.nqb * (SPLIT ? p.nsplit : 1);
   int bh = bid / per_bh;
   const int rem = bid - bh * per_bh;
-  const int split = SPLIT ? rem / p.nqb : 0;
+  int split = SPLIT ? rem / p.nqb : 0;
   int qbr = rem - split * p.nqb;
+  if (CAUSAL && SPLIT && p.lf == 2) {
+    // Rank-major over (rank, head, partition): hardware workgroup b, dealt
+    // to the XCDs in turn, so every XCD runs every eighth entry of the list
+    // sorted longest first (see rank_major).
+    const int per_rank = gridDim.x / p.nqb;
+    const int b = blockIdx.x;
+    qbr = b / per_rank;
+    bh = (b - qbr * per_rank) / p.nsplit;
+    split = b - qbr * per_rank - bh * p.nsplit;
+  }
   if (CAUSAL && !SPLIT && p.lf) {
     const BlockPos bp = longest_first(bid, gridDim.x, p.nqb);
     bh = bp.bh;
@@ -154,8 +168,17 @@ void fwd_kernel(FwdParams p) {
   // Tiles [tile0, tile1) of this workgroup: the partition's share of them.
   int tile0 = 0, tile1 = (kend + C::kBK - 1) / C::kBK;
   if (SPLIT) {
-    tile0 = split * p.tps;
-    tile1 = min(tile1, tile0 + p.tps);
+    // Causal grids of more than one round (lf 2): the block's own range in
+    // nsplit equal runs, so that all of a block's partitions are about
+    // equally long and the rank-major order balances them (a block with
+    // fewer tiles than partitions leaves the last ones empty; their states
+    // weigh 0).  Within one round every partition runs at once and the
+    // longest block's runs are as long either way; there the fixed runs of
+    // tps tiles leave fewer workgroups with a tile or two (C2's forward,
+    // 8 partitions: 0.041 against 0.042 ms).
+    const int len = (CAUSAL && p.lf == 2) ? (tile1 + p.nsplit - 1) / p.nsplit : p.tps;
+    tile0 = split * len;
+    tile1 = min(tile1, tile0 + len);
   }
   const int ntiles = max(tile1 - tile0, 0);
   // Per 32-query block j of the wave: the lane's last key, and the smallest
@@ -570,7 +593,12 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   p.nsplit = split ? a.splits : 1;
   p.tps = (total_tiles + p.nsplit - 1) / p.nsplit;
   p.part = a.part;
-  p.lf = (CAUSAL && !split && fwd_longest_first((long long)p.nqb * a.bh, p.nqb)) ? 1 : 0;
+  // Causal grids with partitions of more than one round (two workgroups per
+  // CU) take the rank-major order: the partitions of a head's long blocks
+  // then spread over every XCD.
+  p.lf = !CAUSAL ? 0
+         : split ? ((long long)p.nqb * a.bh * p.nsplit > 2 * 256 ? 2 : 0)
+                 : (fwd_longest_first((long long)p.nqb * a.bh, p.nqb) ? 1 : 0);
   const long long blocks = (long long)p.nqb * a.bh * p.nsplit;
   if (blocks == 0) return hipSuccess;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;

@@ -118,8 +118,10 @@ size_t streamkl_fwd_workspace_size(int B, int H, int N_Q, int N_K, int d,
  * `splits` workgroups per query block ("Ottimizzazioni del Kernel GPU",
  * Split-K bullet: for small query counts the keys are partitioned across
  * thread blocks to fill the machine).  Partition s folds key tiles
- * [s*T, (s+1)*T), T = ceil(ceil(N_K / tile) / splits), into the five running
- * scalars of each row and stores them in `workspace`; a second kernel merges
+ * [s*T, (s+1)*T), T = ceil(ceil(N_K / tile) / splits) (causal grids of more
+ * than one round of workgroups: T = ceil(t / splits), t the query block's
+ * own admissible tiles), into the five running scalars of each row and
+ * stores them in `workspace`; a second kernel merges
  * the partitions with the same rescale as the online update
  * (m = max m_s, l = sum l_s exp(m_s - m), acc = sum acc_s exp(m1_s - m1)) and
  * finalises kl, lse1, lse2.  Results equal streamkl_fwd's up to the order of

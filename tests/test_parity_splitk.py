@@ -86,6 +86,30 @@ def test_partition_count_changes_only_rounding():
             assert err < 2e-5, f"splits={s} {name}: max |diff| {err}"
 
 
+@pytest.mark.parametrize("case", [(1, 8, 4096, 4096, 64, 8), (2, 3, 3000, 3100, 128, 16), (1, 5, 2500, 2500, 64, 40)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_causal_partitions_in_rank_major_order(case):
+    """Causal grids with partitions of more than one round of workgroups take
+    the rank-major order, each query block's own range cut into runs of equal
+    length: every row of every head against the oracle (40 partitions leave
+    the short blocks' last runs empty)."""
+    B, H, NQ, NK, d, splits = case
+    log(f"causal rank-major partitions {case}")
+    assert ((NQ + 255) // 256) * B * H * splits > 2 * 256  # more than one round: the rank-major order
+    q1, k1, q2, k2 = make_inputs(B, H, NQ, NK, d, torch.bfloat16, "student", 0.3, seed=NQ + splits, device=DEV)
+    scale = d ** -0.5
+    kl, l1, l2 = splitk_raw(q1, k1, q2, k2, scale, True, splits)
+    one = splitk_raw(q1, k1, q2, k2, scale, True, 1)
+    ref = oracle_heads(q1, k1, q2, k2, scale, True, range(B * H))
+    for hh in range(B * H):
+        b, h = divmod(hh, H)
+        for name, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
+            check_rows(to64(got[b, h]), ref[hh][name], q1.dtype, f"{case} head {hh} {name}")
+    for x, y, name in zip((kl, l1, l2), one, ("kl", "lse1", "lse2")):
+        err = (x.double() - y.double()).abs().max().item()
+        assert err < 2e-5, f"{case} {name}: max |diff| against one partition {err}"
+
+
 def test_default_partitioning():
     """Short query blocks over long keys are split; full grids are not."""
     c4, h = WORKLOADS["c4"], WORKLOADS["h32k"]
