@@ -8,6 +8,9 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstreamkl.so")
+# The same sources built with -DSTREAMKL_DEBUG (bounds-checked accesses,
+# plus streamkl_debug_take); tests load it with load(DEBUG_LIB_PATH).
+DEBUG_LIB_PATH = os.path.join(HERE, "libstreamkl_debug.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
@@ -83,6 +86,9 @@ def load(path: str = None):
     lib.streamkl_status_str.restype = ctypes.c_char_p
     lib.streamkl_abi_version.argtypes = []
     lib.streamkl_abi_version.restype = _i
+    if hasattr(lib, "streamkl_debug_take"):  # debug builds only
+        lib.streamkl_debug_take.argtypes = []
+        lib.streamkl_debug_take.restype = ctypes.c_uint
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -94,6 +100,23 @@ def status_str(status: int) -> str:
 
 def abi_version() -> int:
     return load().streamkl_abi_version()
+
+
+def debug_take(lib) -> int:
+    """streamkl_debug_take of a debug build ``lib`` (from load(DEBUG_LIB_PATH)):
+    the first out-of-range access its kernels met since the last call, as
+    (file << 16) | line, or 0; synchronises the device."""
+    return int(lib.streamkl_debug_take())
+
+
+def debug_site(code: int) -> str:
+    """Readable form of a streamkl_debug_take code."""
+    files = {1: "streamkl_fwd.hip", 2: "streamkl_bwd.h", 3: "streamkl_bwd_fused.hip"}
+    if code == 0:
+        return "none"
+    if code == 0xFFFFFFFF:
+        return "device not readable"
+    return f"{files.get(code >> 16, f'file {code >> 16}')}:{code & 0xFFFF}"
 
 
 def fwd(q1, k1, q2, k2, B, H, NQ, NK, d, scale, causal, dtype, kl, lse1, lse2, stream):

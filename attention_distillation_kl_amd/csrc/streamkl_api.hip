@@ -51,6 +51,16 @@ const char *streamkl_status_str(int status) {
 
 int streamkl_abi_version(void) { return 1; }
 
+#ifdef STREAMKL_DEBUG
+unsigned streamkl_debug_take(void) {
+  const unsigned w[] = {streamkl::dbg_take_fwd(), streamkl::dbg_take_bwd_dk(), streamkl::dbg_take_bwd_dq(),
+                        streamkl::dbg_take_bwd_fused()};
+  for (unsigned x : w)
+    if (x) return x;
+  return 0;
+}
+#endif
+
 streamkl_status streamkl_fwd(const void *q1, const void *k1, const void *q2, const void *k2, int B, int H,
                              int N_Q, int N_K, int d, float scale, int causal, int dtype, float *kl,
                              float *lse1, float *lse2, void *stream) {

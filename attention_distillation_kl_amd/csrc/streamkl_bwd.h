@@ -121,6 +121,12 @@ struct BwdParams {
   // heads (lf 1, longest_first) or over the whole grid (lf 2, rank_major)
   // instead of head by head (0).
   int lf;
+#ifdef STREAMKL_DEBUG
+  // Bytes of a query tensor, a key tensor, a row vector and the partial sums
+  // (both gradients', from part_lo).
+  size_t xq, xk, xr, xp;
+  const float *part_lo;
+#endif
 };
 
 // Per-row constants of the recompute.
@@ -141,8 +147,9 @@ struct RowCst {
 __device__ __forceinline__ RowCst row_constants(const BwdParams &p, size_t i, bool valid) {
   RowCst r{INFINITY, INFINITY, 0.f, 0.f};
   if (valid) {
-    const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
-    r.g = p.dkl ? p.dkl[i] : 1.f;
+    const float lse1 = *SK_G(&p.lse1[i], 4, p.lse1, p.xr, 2), lse2 = *SK_G(&p.lse2[i], 4, p.lse2, p.xr, 2);
+    const float kl = *SK_G(&p.kl[i], 4, p.kl, p.xr, 2);
+    r.g = p.dkl ? *SK_G(&p.dkl[i], 4, p.dkl, p.xr, 2) : 1.f;
     r.l1 = lse1 * kLog2e;
     r.l2 = lse2 * kLog2e;
     r.dp = (kl + lse1 - lse2) * p.inv_scale;
@@ -241,6 +248,12 @@ void bwd_kernel(BwdParams p) {
   const int s0 = sblk * C::kBS;
   const int w0 = s0 + wrow * 32;
   const int srow = w0 + col;
+#ifdef STREAMKL_DEBUG
+  // Extents of the stationary and streamed tensors, and of the dynamic LDS.
+  const size_t xS = ROLE == ROLE_DQ ? p.xq : p.xk, xT = ROLE == ROLE_DQ ? p.xk : p.xq;
+  const char *T1 = ROLE == ROLE_DQ ? p.k1 : p.q1, *T2 = ROLE == ROLE_DQ ? p.k2 : p.q2;
+  constexpr size_t kDyn = size_t(2 * C::kStage + C::kXChunks) * 16 + 2 * C::kNCst * C::kBT * 4;
+#endif
 
   // Stationary fragments (B operand of the score products): the student's in
   // registers; the teacher's in registers or, with kX1Lds, in the LDS tile
@@ -253,8 +266,8 @@ void bwd_kernel(BwdParams p) {
     const u32x4 *r2 = reinterpret_cast<const u32x4 *>(X2 + xoff + size_t(srow) * G::kRowBytes);
 #pragma unroll
     for (int c = 0; c < G::kLaneChunks; ++c) {
-      if (!C::kX1Lds) xf1[c] = r1[frag_chunk<BF16, D>(h, c)];
-      xf2[c] = r2[frag_chunk<BF16, D>(h, c)];
+      if (!C::kX1Lds) xf1[c] = *SK_G((&r1[frag_chunk<BF16, D>(h, c)]), 16, X1, xS, 2);
+      xf2[c] = *SK_G((&r2[frag_chunk<BF16, D>(h, c)]), 16, X2, xS, 2);
     }
   } else {
 #pragma unroll
@@ -271,7 +284,8 @@ void bwd_kernel(BwdParams p) {
       const int row = pos / G::kChunks;
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const int r = min(s0 + row, ns - 1);
-      dma16(X1 + xoff + size_t(r) * G::kRowBytes + ch * 16, xtile + i * C::kThreads + wave * 64);
+      dma16(SK_G(X1 + xoff + size_t(r) * G::kRowBytes + ch * 16, 16, X1, xS, 2),
+            SK_L(xtile + i * C::kThreads + wave * 64, 1024, lds, kDyn, 2));
     }
   }
 
@@ -327,6 +341,12 @@ void bwd_kernel(BwdParams p) {
         const int row = pos / G::kChunks;
         const int ch = swz<G::kChunks>(row, pos % G::kChunks);
         const uint32_t o = uint32_t(tile * C::kBT + row) * G::kRowBytes + uint32_t(ch * 16);
+#ifdef STREAMKL_DEBUG
+        // Checked copies are issued through the builtin; the explicit waits
+        // of the unseen form stay in place.
+        dma16(SK_G(Y1 + o, 16, T1, xT, 2), SK_L(wbase + i * C::kThreads, 1024, lds, kDyn, 2));
+        dma16(SK_G(Y2 + o, 16, T2, xT, 2), SK_L(wbase + i * C::kThreads + C::kOffY2, 1024, lds, kDyn, 2));
+#else
         if constexpr (kUnseen) {
           dma16_unseen(Y1, o, wbase + i * C::kThreads);
           dma16_unseen(Y2, o, wbase + i * C::kThreads + C::kOffY2);
@@ -334,6 +354,7 @@ void bwd_kernel(BwdParams p) {
           dma16(Y1 + o, wbase + i * C::kThreads);
           dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
         }
+#endif
       }
     } else {
 #pragma unroll
@@ -343,8 +364,8 @@ void bwd_kernel(BwdParams p) {
         const int ch = swz<G::kChunks>(row, pos % G::kChunks);
         const int r = min(tile * C::kBT + row, nt - 1);
         const size_t o = size_t(r) * G::kRowBytes + ch * 16;
-        dma16(Y1 + o, wbase + i * C::kThreads);
-        dma16(Y2 + o, wbase + i * C::kThreads + C::kOffY2);
+        dma16(SK_G(Y1 + o, 16, T1, xT, 2), SK_L(wbase + i * C::kThreads, 1024, lds, kDyn, 2));
+        dma16(SK_G(Y2 + o, 16, T2, xT, 2), SK_L(wbase + i * C::kThreads + C::kOffY2, 1024, lds, kDyn, 2));
       }
     }
   };
@@ -359,17 +380,17 @@ void bwd_kernel(BwdParams p) {
       n_ok = row < p.nq;
       if (n_ok) {
         const size_t i = size_t(bh) * p.nq + row;
-        n_lse1 = p.lse1[i];
-        n_lse2 = p.lse2[i];
-        n_kl = p.kl[i];
-        n_g = p.dkl ? p.dkl[i] : 1.f;
+        n_lse1 = *SK_G(&p.lse1[i], 4, p.lse1, p.xr, 2);
+        n_lse2 = *SK_G(&p.lse2[i], 4, p.lse2, p.xr, 2);
+        n_kl = *SK_G(&p.kl[i], 4, p.kl, p.xr, 2);
+        n_g = p.dkl ? *SK_G(&p.dkl[i], 4, p.dkl, p.xr, 2) : 1.f;
       }
     }
   };
   auto cstore = [&](int stage) {
     if (ROLE == ROLE_DK && tid < C::kBT) {
       // Rows past N_Q: -1e30 (not -inf) keeps s1' - s2'' finite (0) and P = 0.
-      float *cst = cstage[stage];
+      float *cst = SK_L(cstage[stage], C::kNCst * C::kBT * 4, lds, kDyn, 2);
       cst[tid] = n_ok ? -n_lse1 * p.inv_scale : -1e30f;
       cst[C::kBT + tid] = n_ok ? (n_kl - n_lse2) * p.inv_scale : -1e30f;
       cst[2 * C::kBT + tid] = n_ok ? n_g : 0.f;
@@ -431,7 +452,7 @@ void bwd_kernel(BwdParams p) {
       issue(tile + 1, stage ^ 1);
     }
     const u32x4 *ybase = stage ? ystage1 : ystage0;
-    const float *cst = cstage[stage];
+    const float *cst = SK_L(cstage[stage], C::kNCst * C::kBT * 4, lds, kDyn, 2);
 
     // Whether block sb holds an inadmissible (streamed, stationary) pair for
     // any lane of this wave: a causal frontier or the end of the streamed rows
@@ -485,8 +506,8 @@ void bwd_kernel(BwdParams p) {
         u32x4 f1[kAhead + 1], f2[kAhead + 1];
         auto frag = [&](int cc) {
           const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<BF16, D>(h, cc));
-          f1[cc % (kAhead + 1)] = ybase[pos];
-          f2[cc % (kAhead + 1)] = ybase[C::kOffY2 + pos];
+          f1[cc % (kAhead + 1)] = *SK_L(&ybase[pos], 16, lds, kDyn, 2);
+          f2[cc % (kAhead + 1)] = *SK_L(&ybase[C::kOffY2 + pos], 16, lds, kDyn, 2);
         };
 #pragma unroll
         for (int cc = 0; cc < kAhead; ++cc) frag(cc);
@@ -513,12 +534,12 @@ void bwd_kernel(BwdParams p) {
           const int fc = frag_chunk<BF16, D>(h, cc);
           const int pos = arow * G::kChunks + swz<G::kChunks>(arow, fc);
           if constexpr (C::kX1Lds) {
-            const u32x4 x1 = xtile[xrow * G::kChunks + swz<G::kChunks>(xrow, fc)];
-            mfma_chunk<BF16>(ybase[pos], x1, s1);
+            const u32x4 x1 = *SK_L((&xtile[xrow * G::kChunks + swz<G::kChunks>(xrow, fc)]), 16, lds, kDyn, 2);
+            mfma_chunk<BF16>(*SK_L(&ybase[pos], 16, lds, kDyn, 2), x1, s1);
           } else {
-            mfma_chunk<BF16>(ybase[pos], xf1[cc], s1);
+            mfma_chunk<BF16>(*SK_L(&ybase[pos], 16, lds, kDyn, 2), xf1[cc], s1);
           }
-          mfma_chunk<BF16>(ybase[C::kOffY2 + pos], xf2[cc], s2);
+          mfma_chunk<BF16>(*SK_L(&ybase[C::kOffY2 + pos], 16, lds, kDyn, 2), xf2[cc], s2);
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -589,7 +610,7 @@ void bwd_kernel(BwdParams p) {
             const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
             const int byte = kPair ? (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2
                                    : trofs[mb][t] + (sb * 32 + 16 * ks) * G::kRowBytes;
-            const u32x2 v = read_tr(yb + byte);
+            const u32x2 v = read_tr(SK_L(yb + byte, 8, lds, kDyn, 2));
             a[2 * t] = v[0];
             a[2 * t + 1] = v[1];
           }
@@ -614,8 +635,12 @@ void bwd_kernel(BwdParams p) {
             for (int j = 0; j < 8; ++j) {
               const int row = sb * 32 + 16 * ks + c_row(j, h);
               const int idx = (row * G::kChunks + swz<G::kChunks>(row, d >> 2)) * 4 + (d & 3);
-              if (kG1) acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf1[idx], E.e1[8 * ks + j], acc1[mb], 0, 0, 0);
-              if (kG2) acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(yf2[idx], E.e2[8 * ks + j], acc2[mb], 0, 0, 0);
+              if (kG1)
+                acc1[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(*SK_L(&yf1[idx], 4, lds, kDyn, 2), E.e1[8 * ks + j],
+                                                                acc1[mb], 0, 0, 0);
+              if (kG2)
+                acc2[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(*SK_L(&yf2[idx], 4, lds, kDyn, 2), E.e2[8 * ks + j],
+                                                                acc2[mb], 0, 0, 0);
             }
           }
       }
@@ -630,7 +655,7 @@ void bwd_kernel(BwdParams p) {
       // Keep the operand of the gradient this wave accumulates; hand the
       // other to the partner, which scored the other block.
       u32x4 mine[2], theirs[2];
-      u32x4 *slot = xch + wave * 128 + lane;
+      u32x4 *slot = SK_L(xch + wave * 128 + lane, 64 * 16 + 16, xch, sizeof(xch), 2);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         mine[ks] = hc ? E.pk2[ks] : E.pk1[ks];
@@ -643,7 +668,7 @@ void bwd_kernel(BwdParams p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const u32x4 *peer = xch + (wave ^ 1) * 128 + lane;
+      const u32x4 *peer = SK_L(xch + (wave ^ 1) * 128 + lane, 64 * 16 + 16, xch, sizeof(xch), 2);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) theirs[ks] = peer[64 * ks];
       // Each wave adds its own block first, so its first products need no
@@ -699,7 +724,10 @@ void bwd_kernel(BwdParams p) {
     const size_t ro = (size_t(bh) * ns + srow) * G::kRowBytes;
     char *O1 = (ROLE == ROLE_DQ ? p.dq1 : p.dk1) + ro;
     char *O2 = (ROLE == ROLE_DQ ? p.dq2 : p.dk2) + ro;
-    auto store = [&](char *O, float f, const f32x16 (&A)[kMB]) {
+#ifdef STREAMKL_DEBUG
+    const char *O1b = ROLE == ROLE_DQ ? p.dq1 : p.dk1, *O2b = ROLE == ROLE_DQ ? p.dq2 : p.dk2;
+#endif
+    auto store = [&](char *O, float f, const f32x16 (&A)[kMB] SK_DBG_ARGS(const char *Obase)) {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -708,9 +736,10 @@ void bwd_kernel(BwdParams p) {
           const float v0 = A[mb][4 * g4] * f, v1 = A[mb][4 * g4 + 1] * f;
           const float v2 = A[mb][4 * g4 + 2] * f, v3 = A[mb][4 * g4 + 3] * f;
           if constexpr (BF16) {
-            *reinterpret_cast<u32x2 *>(O + d0 * 2) = u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+            if (SK_OK(O + d0 * 2, 8, Obase, xS, 2))
+              *reinterpret_cast<u32x2 *>(O + d0 * 2) = u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
           } else {
-            *reinterpret_cast<f32x4 *>(O + d0 * 4) = f32x4{v0, v1, v2, v3};
+            if (SK_OK(O + d0 * 4, 16, Obase, xS, 2)) *reinterpret_cast<f32x4 *>(O + d0 * 4) = f32x4{v0, v1, v2, v3};
           }
         }
     };
@@ -722,19 +751,20 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d0 = mb * 32 + g4 * 8 + 4 * h;
-          *reinterpret_cast<f32x4 *>(row + d0) =
-              f32x4{A[mb][4 * g4] * f, A[mb][4 * g4 + 1] * f, A[mb][4 * g4 + 2] * f, A[mb][4 * g4 + 3] * f};
+          if (SK_OK(row + d0, 16, p.part_lo, p.xp, 2))
+            *reinterpret_cast<f32x4 *>(row + d0) =
+                f32x4{A[mb][4 * g4] * f, A[mb][4 * g4 + 1] * f, A[mb][4 * g4 + 2] * f, A[mb][4 * g4 + 3] * f};
         }
     };
     if constexpr (kPair) {
       if (SPLIT) store_part(half ? p.part2 : p.part1, half ? f2 : f1, acc1);
-      else store(half ? O2 : O1, half ? f2 : f1, acc1);
+      else store(half ? O2 : O1, half ? f2 : f1, acc1 SK_DBG_ARGS(half ? O2b : O1b));
     } else if (SPLIT) {
       if (kG1) store_part(p.part1, f1, acc1);
       if (kG2) store_part(p.part2, f2, acc2);
     } else {
-      if (kG1) store(O1, f1, acc1);
-      if (kG2) store(O2, f2, acc2);
+      if (kG1) store(O1, f1, acc1 SK_DBG_ARGS(O1b));
+      if (kG2) store(O2, f2, acc2 SK_DBG_ARGS(O2b));
     }
   }
 }
@@ -747,21 +777,22 @@ void bwd_kernel(BwdParams p) {
 template <bool BF16, int ROLE>
 __global__ __launch_bounds__(256) void part_reduce_kernel(const float *__restrict__ part0, char *out0,
                                                         const float *__restrict__ part1, char *out1, int nsplit,
-                                                        size_t n4) {
+                                                        size_t n4 SK_DBG_ARGS(const float *plo, size_t xp)) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
   const float *part = blockIdx.y ? part1 : part0;
   char *out = blockIdx.y ? out1 : out0;
   const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + i;
-  f32x4 acc = src[0];
+  f32x4 acc = *SK_G(src, 16, plo, xp, 2);
   for (int s = 1; s < nsplit; ++s) {
-    const f32x4 v = src[size_t(s) * n4];
+    const f32x4 v = *SK_G(&src[size_t(s) * n4], 16, plo, xp, 2);
     acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
   }
   if constexpr (BF16) {
-    reinterpret_cast<u32x2 *>(out)[i] = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    if (SK_OK(reinterpret_cast<u32x2 *>(out) + i, 8, out, n4 * 8, 2))
+      reinterpret_cast<u32x2 *>(out)[i] = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
   } else {
-    reinterpret_cast<f32x4 *>(out)[i] = acc;
+    if (SK_OK(reinterpret_cast<f32x4 *>(out) + i, 16, out, n4 * 16, 2)) reinterpret_cast<f32x4 *>(out)[i] = acc;
   }
 }
 
@@ -796,6 +827,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const size_t part_elems = size_t(a.bh) * ns * D * p.nsplit;  // per requested gradient
   p.part1 = split ? a.part : nullptr;
   p.part2 = split ? a.part + ((MASK & 1) ? part_elems : 0) : nullptr;
+#ifdef STREAMKL_DEBUG
+  p.xq = size_t(a.bh) * a.nq * C::G::kRowBytes;
+  p.xk = size_t(a.bh) * a.nk * C::G::kRowBytes;
+  p.xr = size_t(a.bh) * a.nq * sizeof(float);
+  p.part_lo = a.part;
+  p.xp = split ? part_elems * (((MASK & 1) ? 1 : 0) + ((MASK & 2) ? 1 : 0)) * sizeof(float) : 0;
+#endif
   // Resident workgroups per XCD: 32 CUs x (4 SIMDs x waves per SIMD / waves).
   constexpr long long kResidentPerXcd = 32LL * (4 * C::kWavesPerEU / C::kWaves);
   const long long nwg_all = (long long)p.nsb * a.bh;
@@ -825,7 +863,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const float *part0 = (MASK & 1) ? p.part1 : p.part2;
   char *out0 = (MASK & 1) ? o1 : o2;
   part_reduce_kernel<BF16, ROLE><<<dim3(unsigned(rblocks), unsigned(ngrad)), dim3(256), 0, stream>>>(
-      part0, out0, p.part2, o2, p.nsplit, n4);
+      part0, out0, p.part2, o2, p.nsplit, n4 SK_DBG_ARGS(p.part_lo, p.xp));
   return hipGetLastError();
 }
 

@@ -60,4 +60,7 @@ size_t bwd_dk_workspace_floats(int bh, int nk, int d, int grad_mask, int splits)
   const int ngrad = ((grad_mask & 1) ? 1 : 0) + ((grad_mask & 2) ? 1 : 0);
   return size_t(splits) * size_t(bh) * size_t(nk) * size_t(d) * size_t(ngrad);
 }
+#ifdef STREAMKL_DEBUG
+unsigned dbg_take_bwd_dk() { return dbg_take(); }
+#endif
 }  // namespace streamkl

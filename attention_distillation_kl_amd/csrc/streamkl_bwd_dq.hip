@@ -51,4 +51,7 @@ size_t bwd_dq_workspace_floats(int bh, int nq, int d, int grad_mask, int splits)
   return size_t(splits) * size_t(bh) * size_t(nq) * size_t(d) * size_t(ngrad);
 }
 
+#ifdef STREAMKL_DEBUG
+unsigned dbg_take_bwd_dq() { return dbg_take(); }
+#endif
 }  // namespace streamkl

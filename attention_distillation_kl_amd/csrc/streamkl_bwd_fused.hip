@@ -110,6 +110,9 @@ struct FusedParams {
   int nq, nk, nsb;    // nsb: stationary blocks per head
   int kbpw;           // key blocks per workgroup (the one-tile form; 1 otherwise)
   float scale, c, inv_scale;
+#ifdef STREAMKL_DEBUG
+  size_t xq, xk, xr, xw;  // bytes of a query tensor, a key tensor, a row vector, one gradient's sums
+#endif
 };
 
 // Byte offset of (key, query) in an e buffer: rows of 64 bf16, 16-byte
@@ -141,6 +144,9 @@ void fused_bwd_kernel(FusedParams p) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int s16 = lane & 15, grp = lane >> 4;
+#ifdef STREAMKL_DEBUG
+  constexpr size_t kDyn = MULTI ? C::kLdsBytesM : C::kLdsBytes;
+#endif
 
   // Workgroup g of a head takes key blocks [g kbpw, min((g + 1) kbpw, nsb)),
   // key block 0 first: with the mask it sees the most queries.
@@ -190,6 +196,12 @@ void fused_bwd_kernel(FusedParams p) {
       const int row = pos / G::kChunks;
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const uint32_t o = uint32_t(min(s0 + row, p.nk - 1) - s0) * G::kRowBytes + ch * 16;
+#ifdef STREAMKL_DEBUG
+      // Checked copies go through the builtin; the unseen form's waits stay.
+      dma16(SK_G(K1 + o, 16, p.k1, p.xk, 3), SK_L(xtile + i * C::kThreads + wave * 64, 1024, lds, kDyn, 3));
+      dma16(SK_G(K2 + o, 16, p.k2, p.xk, 3),
+            SK_L(xtile + C::kXChunks + i * C::kThreads + wave * 64, 1024, lds, kDyn, 3));
+#else
       if constexpr (decltype(unseen_c)::value) {
         dma16_unseen(K1, o, xtile + i * C::kThreads + wave * 64);
         dma16_unseen(K2, o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
@@ -197,6 +209,7 @@ void fused_bwd_kernel(FusedParams p) {
         dma16(K1 + o, xtile + i * C::kThreads + wave * 64);
         dma16(K2 + o, xtile + C::kXChunks + i * C::kThreads + wave * 64);
       }
+#endif
     }
   };
 
@@ -208,8 +221,8 @@ void fused_bwd_kernel(FusedParams p) {
       const int row = pos / G::kChunks;
       const int ch = swz<G::kChunks>(row, pos % G::kChunks);
       const size_t o = size_t(min(tile * C::kBT + row, p.nq - 1)) * G::kRowBytes + ch * 16;
-      dma16(Y1 + o, wbase + i * C::kThreads);
-      dma16(Y2 + o, wbase + i * C::kThreads + C::kTileChunks);
+      dma16(SK_G(Y1 + o, 16, p.q1, p.xq, 3), SK_L(wbase + i * C::kThreads, 1024, lds, kDyn, 3));
+      dma16(SK_G(Y2 + o, 16, p.q2, p.xq, 3), SK_L(wbase + i * C::kThreads + C::kTileChunks, 1024, lds, kDyn, 3));
     }
   };
   // Per-row constants of a query tile (see the header comment), written by
@@ -217,13 +230,14 @@ void fused_bwd_kernel(FusedParams p) {
   auto cwrite = [&](int tile, int stage) {
     if (tid < C::kBT) {
       const int row = tile * C::kBT + tid;
-      float *cst = cstage[stage];
+      float *cst = SK_L(cstage[stage], 4 * C::kBT * 4, lds, kDyn, 3);
       if (row < p.nq) {
         const size_t i = size_t(bh) * p.nq + row;
-        const float lse1 = p.lse1[i], lse2 = p.lse2[i], kl = p.kl[i];
+        const float lse1 = *SK_G(&p.lse1[i], 4, p.lse1, p.xr, 3), lse2 = *SK_G(&p.lse2[i], 4, p.lse2, p.xr, 3);
+        const float kl = *SK_G(&p.kl[i], 4, p.kl, p.xr, 3);
         cst[tid] = -lse1 * p.inv_scale;
         cst[C::kBT + tid] = (kl - lse2) * p.inv_scale;
-        cst[2 * C::kBT + tid] = p.dkl ? p.dkl[i] : 1.f;
+        cst[2 * C::kBT + tid] = p.dkl ? *SK_G(&p.dkl[i], 4, p.dkl, p.xr, 3) : 1.f;
         cst[3 * C::kBT + tid] = -kl * p.inv_scale * p.c;
       } else {  // rows past N_Q: P = 0 and s1' - s2'' = 0
         cst[tid] = -1e30f;
@@ -250,8 +264,8 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
     for (int cc = 0; cc < G::kLaneChunks; ++cc) {
       const int pos = xrow * G::kChunks + swz<G::kChunks>(xrow, frag_chunk<true, D>(h, cc));
-      xf1[cc] = xtile[pos];
-      xf2[cc] = xtile[C::kXChunks + pos];
+      xf1[cc] = *SK_L(&xtile[pos], 16, lds, kDyn, 3);
+      xf2[cc] = *SK_L(&xtile[C::kXChunks + pos], 16, lds, kDyn, 3);
     }
     const int d0 = mb * 32 + 16 * (grp & 1) + 4 * (s16 & 3);
 #pragma unroll
@@ -261,12 +275,12 @@ void fused_bwd_kernel(FusedParams p) {
         const int row = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
         const int byte = (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2;
         if (kG1) {
-          const u32x2 v = read_tr(reinterpret_cast<const char *>(xtile) + byte);
+          const u32x2 v = read_tr(SK_L(reinterpret_cast<const char *>(xtile) + byte, 8, lds, kDyn, 3));
           kt1[ks][2 * t] = v[0];
           kt1[ks][2 * t + 1] = v[1];
         }
         if (kG2) {
-          const u32x2 v = read_tr(reinterpret_cast<const char *>(xtile + C::kXChunks) + byte);
+          const u32x2 v = read_tr(SK_L(reinterpret_cast<const char *>(xtile + C::kXChunks) + byte, 8, lds, kDyn, 3));
           kt2[ks][2 * t] = v[0];
           kt2[ks][2 * t + 1] = v[1];
         }
@@ -322,8 +336,8 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
         for (int cc = 0; cc < G::kLaneChunks; ++cc) {
           const int pos = arow * G::kChunks + swz<G::kChunks>(arow, frag_chunk<true, D>(h, cc));
-          mfma_chunk<true>(ybase[pos], xf1[cc], s1);
-          mfma_chunk<true>(ybase[C::kTileChunks + pos], xf2[cc], s2);
+          mfma_chunk<true>(*SK_L(&ybase[pos], 16, lds, kDyn, 3), xf1[cc], s1);
+          mfma_chunk<true>(*SK_L(&ybase[C::kTileChunks + pos], 16, lds, kDyn, 3), xf2[cc], s2);
         }
       }
       // 2. e1, e2 packed to bf16: pk[ks][w] holds rows c_row(8ks + 2w, h)
@@ -373,7 +387,7 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int row = sb * 32 + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
-              const u32x2 v = read_tr(yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2);
+              const u32x2 v = read_tr(SK_L((yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2), 8, lds, kDyn, 3));
               a[2 * t] = v[0];
               a[2 * t + 1] = v[1];
             }
@@ -399,8 +413,11 @@ void fused_bwd_kernel(FusedParams p) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int q = sb * 32 + 8 * g4 + 4 * h;
           const int ks = g4 >> 1, w = 2 * (g4 & 1);
-          if (kG1) *reinterpret_cast<u32x2 *>(ebuf + ebyte(key, q)) = u32x2{pk1[ks][w], pk1[ks][w + 1]};
-          if (kG2) *reinterpret_cast<u32x2 *>(ebuf + C::kEBytes + ebyte(key, q)) = u32x2{pk2[ks][w], pk2[ks][w + 1]};
+          if (kG1)
+            *reinterpret_cast<u32x2 *>(SK_L(ebuf + ebyte(key, q), 8, lds, kDyn, 3)) = u32x2{pk1[ks][w], pk1[ks][w + 1]};
+          if (kG2)
+            *reinterpret_cast<u32x2 *>(SK_L(ebuf + C::kEBytes + ebyte(key, q), 8, lds, kDyn, 3)) =
+                u32x2{pk2[ks][w], pk2[ks][w + 1]};
         }
       }
     }
@@ -419,7 +436,7 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int key = kg * C::kGroupKeys + 16 * ks + 8 * t + 4 * h + (s16 >> 2);
-        const u32x2 v = read_tr(eb + ebyte(key, qa));
+        const u32x2 v = read_tr(SK_L(eb + ebyte(key, qa), 8, lds, kDyn, 3));
         e[2 * t] = v[0];
         e[2 * t + 1] = v[1];
       }
@@ -440,7 +457,7 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = c_row(r, h);
-      if (qb + q < p.nq) unsafeAtomicAdd(base + size_t(q) * D, a[r]);
+      if (qb + q < p.nq && SK_OK(base + size_t(q) * D, 4, ws, p.xw, 3)) unsafeAtomicAdd(base + size_t(q) * D, a[r]);
     }
   };
   auto tile_dq = [&](int tile) {
@@ -463,7 +480,8 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d0 = m * 32 + g4 * 8 + 4 * h;
-          *reinterpret_cast<u32x2 *>(O + ro + d0 * 2) =
+          if (SK_OK(O + ro + d0 * 2, 8, O, p.xk, 3))
+            *reinterpret_cast<u32x2 *>(O + ro + d0 * 2) =
               u32x2{pack_bf16(A[m][4 * g4] * f, A[m][4 * g4 + 1] * f), pack_bf16(A[m][4 * g4 + 2] * f, A[m][4 * g4 + 3] * f)};
         }
     };
@@ -496,7 +514,7 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
               for (int tt = 0; tt < 2; ++tt) {
                 const int row = sb * 32 + 16 * ks + 8 * tt + 4 * h + (s16 >> 2);
-                const u32x2 v = read_tr(yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2);
+                const u32x2 v = read_tr(SK_L((yb + (row * G::kChunks + swz<G::kChunks>(row, d0 >> 3)) * 16 + (d0 & 7) * 2), 8, lds, kDyn, 3));
                 fq[2 * tt] = v[0];
                 fq[2 * tt + 1] = v[1];
               }
@@ -510,7 +528,8 @@ void fused_bwd_kernel(FusedParams p) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               const int dc = (mp + j) * 32 + g4 * 8 + 4 * h;
-              *reinterpret_cast<u32x2 *>(O + ro + dc * 2) =
+              if (SK_OK(O + ro + dc * 2, 8, O, p.xk, 3))
+                *reinterpret_cast<u32x2 *>(O + ro + dc * 2) =
                   u32x2{pack_bf16(a[j][4 * g4] * f, a[j][4 * g4 + 1] * f), pack_bf16(a[j][4 * g4 + 2] * f, a[j][4 * g4 + 3] * f)};
             }
         }
@@ -606,20 +625,21 @@ void fused_bwd_kernel(FusedParams p) {
 
 // Zeroes n4 float4 values.
 __global__ __launch_bounds__(256) void zero_kernel(f32x4 *x, size_t n4) {
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256) x[i] = f32x4{};
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256)
+    if (SK_OK(x + i, 16, x, n4 * 16, 3)) x[i] = f32x4{};
 }
 
 // dq = f * ws, fp32 -> bf16 (nearest even); 4 values per thread.  blockIdx.y
 // picks the gradient, so both requested gradients take one launch.
 __global__ __launch_bounds__(256) void convert_kernel(const f32x4 *ws0, float f0, u32x2 *out0, const f32x4 *ws1,
-                                                      float f1, u32x2 *out1, size_t n4) {
+                                                      float f1, u32x2 *out1, size_t n4 SK_DBG_ARGS(size_t xw)) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
   const f32x4 *ws = blockIdx.y ? ws1 : ws0;
   const float f = blockIdx.y ? f1 : f0;
   u32x2 *out = blockIdx.y ? out1 : out0;
-  const f32x4 v = ws[i];
-  out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
+  const f32x4 v = *SK_G(&ws[i], 16, ws, xw, 3);
+  if (SK_OK(out + i, 8, out, n4 * 8, 3)) out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
 }
 
 template <int D, bool CAUSAL, int MASK, bool GSIGN>
@@ -655,6 +675,12 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
   p.scale = a.scale;
   p.c = float(double(a.scale) * 1.4426950408889634);
   p.inv_scale = float(1.0 / double(a.scale));
+#ifdef STREAMKL_DEBUG
+  p.xq = size_t(a.bh) * a.nq * C::G::kRowBytes;
+  p.xk = size_t(a.bh) * a.nk * C::G::kRowBytes;
+  p.xr = size_t(a.bh) * a.nq * sizeof(float);
+  p.xw = n * sizeof(float);
+#endif
   const int ngrad = ((MASK & 1) ? 1 : 0) + ((MASK & 2) ? 1 : 0);
   const size_t n4 = n / 4;  // D is a multiple of 4
   if (n4 > 0) {
@@ -683,7 +709,8 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
     const float f0 = (MASK & 1) ? a.scale * a.scale : a.scale;
     u32x2 *o0 = static_cast<u32x2 *>((MASK & 1) ? a.dq1 : a.dq2);
     convert_kernel<<<dim3(unsigned(cb), unsigned(ngrad)), dim3(256), 0, stream>>>(
-        w0, f0, o0, reinterpret_cast<const f32x4 *>(p.ws2), a.scale, static_cast<u32x2 *>(a.dq2), n4);
+        w0, f0, o0, reinterpret_cast<const f32x4 *>(p.ws2), a.scale, static_cast<u32x2 *>(a.dq2),
+        n4 SK_DBG_ARGS(n * sizeof(float)));
   }
   return hipGetLastError();
 }
@@ -712,4 +739,7 @@ hipError_t launch_bwd_fused(const BwdArgs &a, float *ws, hipStream_t stream) {
   return a.causal ? launch_fused_masks<128, true>(a, ws, stream) : launch_fused_masks<128, false>(a, ws, stream);
 }
 
+#ifdef STREAMKL_DEBUG
+unsigned dbg_take_bwd_fused() { return dbg_take(); }
+#endif
 }  // namespace streamkl

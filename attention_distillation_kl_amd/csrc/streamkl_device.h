@@ -200,4 +200,57 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// ------------------------------------------------------------ debug build
+// Built with -DSTREAMKL_DEBUG, every global-memory access of the kernels, and
+// the LDS accesses of their tile loops, are checked against the extent of
+// the buffer they belong to (the extents travel in the kernels' parameters).
+// An access found outside its buffer is not made: a global load or copy
+// reads a zeroed dummy line instead, an LDS access goes to the start of the
+// workgroup's LDS, a store or atomic is dropped.  The site of the first such
+// access, (file id << 16) | line, is kept in dbg_word -- one per translation
+// unit -- for the host to collect (dbg_take).  Without the macro, SK_G and
+// SK_L return their pointer and SK_OK is true, so a release build compiles
+// to the same instructions as the code without the checks.
+// File ids: 1 streamkl_fwd.hip, 2 streamkl_bwd.h, 3 streamkl_bwd_fused.hip.
+__host__ __device__ inline bool dbg_in(uintptr_t a, size_t n, uintptr_t lo, size_t bytes) {
+  return a >= lo && a - lo <= bytes && n <= bytes - (a - lo);
+}
+#ifdef STREAMKL_DEBUG
+static __device__ unsigned int dbg_word;
+static __device__ __align__(16) u32x4 dbg_dummy[4];
+__device__ __forceinline__ bool dbg_ok(const void *p, size_t n, const void *lo, size_t bytes, unsigned site) {
+  const bool ok = dbg_in(uintptr_t(p), n, uintptr_t(lo), bytes);
+  if (!ok) atomicCAS(&dbg_word, 0u, site);
+  return ok;
+}
+template <class T>
+__device__ __forceinline__ T *dbg_global(T *p, size_t n, const void *lo, size_t bytes, unsigned site) {
+  return dbg_ok(p, n, lo, bytes, site) ? p : reinterpret_cast<T *>(dbg_dummy);
+}
+template <class T>
+__device__ __forceinline__ T *dbg_lds(T *p, size_t n, const void *lo, size_t bytes, unsigned site) {
+  return dbg_ok(p, n, lo, bytes, site) ? p : (T *)(lo);
+}
+// The first violation recorded by this translation unit's kernels since the
+// last call (0: none), then cleared.  Synchronises the device.
+static inline unsigned dbg_take() {
+  unsigned w = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return ~0u;
+  if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(dbg_word), sizeof(w)) != hipSuccess) return ~0u;
+  const unsigned z = 0;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof(z)) != hipSuccess) return ~0u;
+  return w;
+}
+#define SK_SITE(file) ((unsigned(file) << 16) | unsigned(__LINE__))
+#define SK_G(p, n, lo, bytes, file) ::streamkl::dbg_global((p), (n), (lo), (bytes), SK_SITE(file))
+#define SK_L(p, n, lo, bytes, file) ::streamkl::dbg_lds((p), (n), (lo), (bytes), SK_SITE(file))
+#define SK_OK(p, n, lo, bytes, file) ::streamkl::dbg_ok((p), (n), (lo), (bytes), SK_SITE(file))
+#define SK_DBG_ARGS(...) , __VA_ARGS__
+#else
+#define SK_G(p, n, lo, bytes, file) (p)
+#define SK_L(p, n, lo, bytes, file) (p)
+#define SK_OK(p, n, lo, bytes, file) true
+#define SK_DBG_ARGS(...)
+#endif
+
 }  // namespace streamkl

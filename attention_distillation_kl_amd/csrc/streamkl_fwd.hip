@@ -80,6 +80,9 @@ struct FwdParams {
   int lf;
   size_t rows;  // B * H * N_Q
   float *part;
+#ifdef STREAMKL_DEBUG
+  size_t xq, xk, xr, xp;  // bytes of a query tensor, a key tensor, a row vector, the partition states
+#endif
 };
 
 // Row-state layout of the split-K workspace: scalar k of partition s for
@@ -152,8 +155,8 @@ void fwd_kernel(FwdParams p) {
       const u32x4 *r2 = reinterpret_cast<const u32x4 *>(p.q2 + qoff + size_t(qrow) * G::kRowBytes);
 #pragma unroll
       for (int c = 0; c < G::kLaneChunks; ++c) {
-        qf1[j][c] = r1[frag_chunk<BF16, D>(h, c)];
-        qf2[j][c] = r2[frag_chunk<BF16, D>(h, c)];
+        qf1[j][c] = *SK_G((&r1[frag_chunk<BF16, D>(h, c)]), 16, p.q1, p.xq, 1);
+        qf2[j][c] = *SK_G((&r2[frag_chunk<BF16, D>(h, c)]), 16, p.q2, p.xq, 1);
       }
     } else {
 #pragma unroll
@@ -222,8 +225,10 @@ void fwd_kernel(FwdParams p) {
         const int row = pos / G::kChunks;
         const int ch = swz<G::kChunks>(row, pos % G::kChunks);
         const size_t o = size_t(min(kt * C::kBK + row, p.nk - 1)) * G::kRowBytes + ch * 16;
-        dma16(kb1 + o, lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64);
-        dma16(kb2 + o, lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64);
+        dma16(SK_G(kb1 + o, 16, p.k1, p.xk, 1),
+              SK_L(lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64, 1024, lds, C::kLdsBytes, 1));
+        dma16(SK_G(kb2 + o, 16, p.k2, p.xk, 1),
+              SK_L(lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64, 1024, lds, C::kLdsBytes, 1));
       }
       return;
     }
@@ -234,8 +239,8 @@ void fwd_kernel(FwdParams p) {
       const int oi = i * (C::kThreads / C::kBK) * 16;
       u32x4 *w1 = lds + (stage * 2 + 0) * C::kTileChunks + i * C::kThreads + wave * 64;
       u32x4 *w2 = lds + (stage * 2 + 1) * C::kTileChunks + i * C::kThreads + wave * 64;
-      dma16(kb1 + o + oi, w1);
-      dma16(kb2 + o + oi, w2);
+      dma16(SK_G(kb1 + o + oi, 16, p.k1, p.xk, 1), SK_L(w1, 1024, lds, C::kLdsBytes, 1));
+      dma16(SK_G(kb2 + o + oi, 16, p.k2, p.xk, 1), SK_L(w2, 1024, lds, C::kLdsBytes, 1));
     }
   };
 
@@ -304,8 +309,8 @@ void fwd_kernel(FwdParams p) {
     for (int cc = 0; cc < G::kLaneChunks; ++cc) {
       const int pos = RM ? row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc))
                          : frag_chunk<BF16, D>(h, cc) * C::kBK + row;
-      mfma_chunk<BF16>(t1[pos], qf1[j][cc], s1);
-      mfma_chunk<BF16>(t2[pos], qf2[j][cc], s2);
+      mfma_chunk<BF16>(*SK_L(&t1[pos], 16, lds, C::kLdsBytes, 1), qf1[j][cc], s1);
+      mfma_chunk<BF16>(*SK_L(&t2[pos], 16, lds, C::kLdsBytes, 1), qf2[j][cc], s2);
     }
   };
   // A raise (rare: the first admissible block of a row, or an overflow)
@@ -361,7 +366,7 @@ void fwd_kernel(FwdParams p) {
       for (int cc = 0; cc < G::kLaneChunks; ++cc) {
         const int pos = RM ? row * G::kChunks + swz<G::kChunks>(row, frag_chunk<BF16, D>(h, cc))
                            : frag_chunk<BF16, D>(h, cc) * C::kBK + row;
-        const u32x4 a1 = b1[pos], a2 = b2[pos];
+        const u32x4 a1 = *SK_L(&b1[pos], 16, lds, C::kLdsBytes, 1), a2 = *SK_L(&b2[pos], 16, lds, C::kLdsBytes, 1);
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
           mfma_chunk<BF16>(a1, qf1[j][cc], s1[j]);
@@ -434,7 +439,8 @@ void fwd_kernel(FwdParams p) {
       // same way, through LDS: the tile buffers are free, since the loop
       // ended in a barrier after its last reads and no copy is in flight.
       static_assert(C::kKSplit == 2 && NQB == 1, "one partner wave, one query block");
-      float *x = reinterpret_cast<float *>(lds) + (wave / 2) * (ST_N * 32) + col;
+      float *x = SK_L(reinterpret_cast<float *>(lds) + (wave / 2) * (ST_N * 32) + col, ((ST_N - 1) * 32 + 1) * 4,
+                      lds, C::kLdsBytes, 1);
       __syncthreads();
       if (ksub == 1 && h == 0) {
         x[ST_M1 * 32] = M1;
@@ -464,11 +470,14 @@ void fwd_kernel(FwdParams p) {
         const size_t r = size_t(bh) * p.nq + qrow;
         float *out = p.part + size_t(split) * p.rows + r;
         const size_t stride = size_t(p.nsplit) * p.rows;
-        out[ST_M1 * stride] = M1;
-        out[ST_M2 * stride] = M2;
-        out[ST_L1 * stride] = L1;
-        out[ST_L2 * stride] = L2;
-        out[ST_ACC * stride] = A;
+        auto put = [&](float *q, float v) {
+          if (SK_OK(q, 4, p.part, p.xp, 1)) *q = v;
+        };
+        put(out + ST_M1 * stride, M1);
+        put(out + ST_M2 * stride, M2);
+        put(out + ST_L1 * stride, L1);
+        put(out + ST_L2 * stride, L2);
+        put(out + ST_ACC * stride, A);
       }
       continue;
     }
@@ -476,9 +485,9 @@ void fwd_kernel(FwdParams p) {
       const float lse1 = M1 * p.scale + logf(L1);
       const float lse2 = M2 * p.scale + logf(L2);
       const size_t o = size_t(bh) * p.nq + qrow;
-      p.kl[o] = p.scale * (A / L1) + lse2 - lse1;
-      p.lse1[o] = lse1;
-      p.lse2[o] = lse2;
+      if (SK_OK(p.kl + o, 4, p.kl, p.xr, 1)) p.kl[o] = p.scale * (A / L1) + lse2 - lse1;
+      if (SK_OK(p.lse1 + o, 4, p.lse1, p.xr, 1)) p.lse1[o] = lse1;
+      if (SK_OK(p.lse2 + o, 4, p.lse2, p.xr, 1)) p.lse2[o] = lse2;
     }
   }
 }
@@ -510,7 +519,8 @@ __device__ __forceinline__ RowState combine(const RowState &a, const RowState &b
 
 template <int G>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part, int nsplit, size_t rows,
-                                                    float scale, float c, float *kl, float *lse1, float *lse2) {
+                                                    float scale, float c, float *kl, float *lse1,
+                                                    float *lse2 SK_DBG_ARGS(size_t xp, size_t xr)) {
   static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "a row's lanes lie in one wave");
   const size_t t = size_t(blockIdx.x) * 256 + threadIdx.x;
   const size_t r = t / G;
@@ -523,8 +533,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
   if (live) {
     for (int k = j; k < nsplit; k += G) {
       const float *st = part + size_t(k) * rows + r;
-      const RowState x{st[ST_M1 * stride], st[ST_M2 * stride], st[ST_L1 * stride], st[ST_L2 * stride],
-                       st[ST_ACC * stride]};
+      const RowState x{*SK_G(&st[ST_M1 * stride], 4, part, xp, 1), *SK_G(&st[ST_M2 * stride], 4, part, xp, 1),
+                       *SK_G(&st[ST_L1 * stride], 4, part, xp, 1), *SK_G(&st[ST_L2 * stride], 4, part, xp, 1),
+                       *SK_G(&st[ST_ACC * stride], 4, part, xp, 1)};
       s = (k == j) ? x : combine(s, x, c);
     }
   }
@@ -537,9 +548,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
   if (live && j == 0) {
     const float l1 = s.m1 * scale + logf(s.l1);
     const float l2 = s.m2 * scale + logf(s.l2);
-    kl[r] = scale * (s.acc / s.l1) + l2 - l1;
-    lse1[r] = l1;
-    lse2[r] = l2;
+    if (SK_OK(kl + r, 4, kl, xr, 1)) kl[r] = scale * (s.acc / s.l1) + l2 - l1;
+    if (SK_OK(lse1 + r, 4, lse1, xr, 1)) lse1[r] = l1;
+    if (SK_OK(lse2 + r, 4, lse2, xr, 1)) lse2[r] = l2;
   }
 }
 
@@ -547,6 +558,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
 // partitions (at most 64 lanes; more partitions are looped over).
 inline hipError_t launch_merge(const float *part, int nsplit, size_t rows, float scale, float c, float *kl,
                                float *lse1, float *lse2, hipStream_t stream) {
+#ifdef STREAMKL_DEBUG
+  const size_t xp = size_t(ST_N) * nsplit * rows * sizeof(float), xr = rows * sizeof(float);
+#endif
   int g = 1;
   while (g < nsplit && g < 64) g *= 2;
   const size_t threads = rows * size_t(g);
@@ -554,13 +568,13 @@ inline hipError_t launch_merge(const float *part, int nsplit, size_t rows, float
   if (blocks > size_t(INT_MAX)) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks)}, block{256u};
   switch (g) {
-    case 1: merge_kernel<1><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    case 2: merge_kernel<2><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    case 4: merge_kernel<4><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    case 8: merge_kernel<8><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    case 16: merge_kernel<16><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    case 32: merge_kernel<32><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
-    default: merge_kernel<64><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2); break;
+    case 1: merge_kernel<1><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    case 2: merge_kernel<2><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    case 4: merge_kernel<4><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    case 8: merge_kernel<8><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    case 16: merge_kernel<16><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    case 32: merge_kernel<32><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
+    default: merge_kernel<64><<<grid, block, 0, stream>>>(part, nsplit, rows, scale, c, kl, lse1, lse2 SK_DBG_ARGS(xp, xr)); break;
   }
   return hipGetLastError();
 }
@@ -593,6 +607,12 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
   p.nsplit = split ? a.splits : 1;
   p.tps = (total_tiles + p.nsplit - 1) / p.nsplit;
   p.part = a.part;
+#ifdef STREAMKL_DEBUG
+  p.xq = size_t(a.bh) * a.nq * C::G::kRowBytes;
+  p.xk = size_t(a.bh) * a.nk * C::G::kRowBytes;
+  p.xr = size_t(a.bh) * a.nq * sizeof(float);
+  p.xp = split ? size_t(ST_N) * p.nsplit * p.rows * sizeof(float) : 0;
+#endif
   // Causal grids with partitions of more than one round (two workgroups per
   // CU) take the rank-major order: the partitions of a head's long blocks
   // then spread over every XCD.
@@ -659,4 +679,7 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
   return a.causal ? launch<false, 128, true>(a, stream) : launch<false, 128, false>(a, stream);
 }
 
+#ifdef STREAMKL_DEBUG
+unsigned dbg_take_fwd() { return dbg_take(); }
+#endif
 }  // namespace streamkl

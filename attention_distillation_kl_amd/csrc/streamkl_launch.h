@@ -74,4 +74,13 @@ hipError_t launch_bwd_dk(const BwdArgs &a, hipStream_t stream);
 size_t bwd_fused_workspace_floats(int bh, int nq, int d, int grad_mask);
 hipError_t launch_bwd_fused(const BwdArgs &a, float *ws, hipStream_t stream);
 
+#ifdef STREAMKL_DEBUG
+// Debug builds: the first out-of-range access recorded by each translation
+// unit's kernels since the last call (0: none), then cleared.
+unsigned dbg_take_fwd();
+unsigned dbg_take_bwd_dk();
+unsigned dbg_take_bwd_dq();
+unsigned dbg_take_bwd_fused();
+#endif
+
 }  // namespace streamkl

@@ -335,6 +335,24 @@ const char *streamkl_status_str(int status);
 /* Version of this ABI (bumped on any incompatible change). */
 int streamkl_abi_version(void);
 
+#ifdef STREAMKL_DEBUG
+/*
+ * streamkl_debug_take -- debug builds only (the library compiled with
+ * -DSTREAMKL_DEBUG, libstreamkl_debug.so); not exported by release builds.
+ * There every global-memory access of the kernels, and the LDS accesses of
+ * their tile loops, are checked against the extent of the buffer they
+ * belong to.  An access found out of range is not made (a global load or
+ * copy reads zeros, an LDS access goes to the start of the workgroup's LDS,
+ * a store or atomic is dropped), so a faulty index cannot fault the GPU; the
+ * kernels keep the site of the first one.  This call waits for the device
+ * (hipDeviceSynchronize), returns that site and clears it: 0 for none, else
+ * (file << 16) | line, with file 1 streamkl_fwd.hip, 2 streamkl_bwd.h,
+ * 3 streamkl_bwd_fused.hip of the library's sources; ~0 when the device
+ * could not be read.  The record is per process, shared by every call.
+ */
+unsigned streamkl_debug_take(void);
+#endif
+
 #ifdef __cplusplus
 }
 #endif
