@@ -777,7 +777,7 @@ void bwd_kernel(BwdParams p) {
 template <bool BF16, int ROLE>
 __global__ __launch_bounds__(256) void part_reduce_kernel(const float *__restrict__ part0, char *out0,
                                                         const float *__restrict__ part1, char *out1, int nsplit,
-                                                        size_t n4 SK_DBG_ARGS(const float *plo, size_t xp)) {
+                                                        size_t n4 SK_DBG_ARGS(const float *plo, size_t xp, size_t xo)) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
   const float *part = blockIdx.y ? part1 : part0;
@@ -789,10 +789,10 @@ __global__ __launch_bounds__(256) void part_reduce_kernel(const float *__restric
     acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
   }
   if constexpr (BF16) {
-    if (SK_OK(reinterpret_cast<u32x2 *>(out) + i, 8, out, n4 * 8, 2))
+    if (SK_OK(reinterpret_cast<u32x2 *>(out) + i, 8, out, xo, 2))
       reinterpret_cast<u32x2 *>(out)[i] = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
   } else {
-    if (SK_OK(reinterpret_cast<f32x4 *>(out) + i, 16, out, n4 * 16, 2)) reinterpret_cast<f32x4 *>(out)[i] = acc;
+    if (SK_OK(reinterpret_cast<f32x4 *>(out) + i, 16, out, xo, 2)) reinterpret_cast<f32x4 *>(out)[i] = acc;
   }
 }
 
@@ -863,7 +863,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const float *part0 = (MASK & 1) ? p.part1 : p.part2;
   char *out0 = (MASK & 1) ? o1 : o2;
   part_reduce_kernel<BF16, ROLE><<<dim3(unsigned(rblocks), unsigned(ngrad)), dim3(256), 0, stream>>>(
-      part0, out0, p.part2, o2, p.nsplit, n4 SK_DBG_ARGS(p.part_lo, p.xp));
+      part0, out0, p.part2, o2, p.nsplit, n4 SK_DBG_ARGS(p.part_lo, p.xp, ROLE == ROLE_DQ ? p.xq : p.xk));
   return hipGetLastError();
 }
 

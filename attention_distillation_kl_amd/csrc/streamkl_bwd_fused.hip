@@ -624,22 +624,22 @@ void fused_bwd_kernel(FusedParams p) {
 }
 
 // Zeroes n4 float4 values.
-__global__ __launch_bounds__(256) void zero_kernel(f32x4 *x, size_t n4) {
+__global__ __launch_bounds__(256) void zero_kernel(f32x4 *x, size_t n4 SK_DBG_ARGS(size_t xw)) {
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += size_t(gridDim.x) * 256)
-    if (SK_OK(x + i, 16, x, n4 * 16, 3)) x[i] = f32x4{};
+    if (SK_OK(x + i, 16, x, xw, 3)) x[i] = f32x4{};
 }
 
 // dq = f * ws, fp32 -> bf16 (nearest even); 4 values per thread.  blockIdx.y
 // picks the gradient, so both requested gradients take one launch.
 __global__ __launch_bounds__(256) void convert_kernel(const f32x4 *ws0, float f0, u32x2 *out0, const f32x4 *ws1,
-                                                      float f1, u32x2 *out1, size_t n4 SK_DBG_ARGS(size_t xw)) {
+                                                      float f1, u32x2 *out1, size_t n4 SK_DBG_ARGS(size_t xw, size_t xo)) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n4) return;
   const f32x4 *ws = blockIdx.y ? ws1 : ws0;
   const float f = blockIdx.y ? f1 : f0;
   u32x2 *out = blockIdx.y ? out1 : out0;
   const f32x4 v = *SK_G(&ws[i], 16, ws, xw, 3);
-  if (SK_OK(out + i, 8, out, n4 * 8, 3)) out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
+  if (SK_OK(out + i, 8, out, xo, 3)) out[i] = u32x2{pack_bf16(v[0] * f, v[1] * f), pack_bf16(v[2] * f, v[3] * f)};
 }
 
 template <int D, bool CAUSAL, int MASK, bool GSIGN>
@@ -685,7 +685,8 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
   const size_t n4 = n / 4;  // D is a multiple of 4
   if (n4 > 0) {
     const size_t zb = std::min<size_t>((n4 * ngrad + 255) / 256, 4096);
-    zero_kernel<<<dim3(unsigned(zb)), dim3(256), 0, stream>>>(reinterpret_cast<f32x4 *>(ws), n4 * ngrad);
+    zero_kernel<<<dim3(unsigned(zb)), dim3(256), 0, stream>>>(reinterpret_cast<f32x4 *>(ws),
+                                                            n4 * ngrad SK_DBG_ARGS(n * ngrad * sizeof(float)));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -710,7 +711,7 @@ hipError_t launch_fused_t(const BwdArgs &a, float *ws, hipStream_t stream) {
     u32x2 *o0 = static_cast<u32x2 *>((MASK & 1) ? a.dq1 : a.dq2);
     convert_kernel<<<dim3(unsigned(cb), unsigned(ngrad)), dim3(256), 0, stream>>>(
         w0, f0, o0, reinterpret_cast<const f32x4 *>(p.ws2), a.scale, static_cast<u32x2 *>(a.dq2),
-        n4 SK_DBG_ARGS(n * sizeof(float)));
+        n4 SK_DBG_ARGS(n * sizeof(float), p.xq));
   }
   return hipGetLastError();
 }
