@@ -105,6 +105,26 @@ def test_fwd_full_size_sampled_rows(name):
     torch.cuda.empty_cache()
 
 
+def test_fwd_c4_whole_heads():
+    """C4 (2048 queries over 65536 keys, non-causal, forward only) in the
+    benchmark's launch configuration -- the library's key partitions and the
+    merge -- with every row of the first and last head compared with the
+    oracle: all eight query blocks and every partition's keys."""
+    w = WORKLOADS["c4"]
+    log("fwd c4 full size, whole first and last heads")
+    q1, k1, q2, k2 = workload_inputs(w, DEV)
+    kl, l1, l2 = ops.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
+    torch.cuda.synchronize()
+    heads = [0, w.B * w.H - 1]
+    ref = oracle_heads(q1, k1, q2, k2, w.scale, w.causal, heads)
+    for hh in heads:
+        b, h = divmod(hh, w.H)
+        for key, got in (("kl", kl), ("lse1", l1), ("lse2", l2)):
+            check_rows(to64(got[b, h]), ref[hh][key], q1.dtype, f"c4 head {hh} {key}")
+    del q1, k1, q2, k2
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_identical_teacher_student_is_exactly_zero(dt, causal):
